@@ -1,0 +1,244 @@
+/*
+ * lrkv.h -- decode attention read directly from a low-rank-compressed KV cache,
+ * for AMD Instinct MI355X (gfx950). Plain C ABI of liblrkv.so.
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *
+ *  - Palu: KV-Cache Compression with Low-Rank Projection (digest), Method details.
+ *    Keys and values are cached as per-token latents h = x A (rank r per unit,
+ *    a unit being a G-LRD group of s heads or, with s = 1, one KV head). At
+ *    decode the keys are rebuilt on chip as K = H^k B^k, RoPE is applied at each
+ *    token's position, and the query attends; the value reconstruction B^v is
+ *    folded into W^o offline, so the output stays in latent space: o = p H^v.
+ *    Without RoPE, B^k is absorbed into the query (q' = q (B^k)^T) and the
+ *    scores are H^k q'. The Hadamard fold (A R)(R^T B) lets the latents be
+ *    stored as int4 (per-token groups of 32, see the Appendix of the digest and
+ *    section 5 of the Shard post for the symmetric [-7, 7] range).
+ *  - PuzzleKV: page-based low-rank decomposition for KV-cache compression,
+ *    section 3.3. Dense sink / local-window pages plus per-page factors
+ *    X_hat = L R (Eq. 2), obtained from the P x P Gram matrix; attention runs
+ *    over dense and factored pages and merges them by online softmax; a page is
+ *    factored once it is full and has left the window.
+ *
+ * Conventions for every entry point:
+ *  - Ownership: the caller owns every buffer (device memory, e.g. PyTorch
+ *    tensors). The library allocates nothing; scratch memory is the caller's
+ *    `workspace`, sized by lrkv_decode_workspace_bytes.
+ *  - Pointers marked "device" must be device memory of the current HIP device.
+ *  - Asynchrony: calls only enqueue kernels on `stream` (a hipStream_t; NULL is
+ *    the default stream) and never synchronise. Results are ready when the
+ *    stream reaches them.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    a failing call returns a negative lrkv_status and leaves device memory
+ *    untouched. A failed kernel launch returns LRKV_ERR_HIP. No C++ exception
+ *    crosses the ABI.
+ *  - Thread safety: calls are re-entrant; the library keeps no global state
+ *    beyond its loaded code objects.
+ *  - Lengths: `lens` (device, int32 [batch]) holds each sequence's current
+ *    number of cached tokens; `host_max_len` is the caller's host-side bound on
+ *    max(lens) (used for capacity checks and grid sizing; it must not be
+ *    smaller than the true maximum).
+ */
+#ifndef LRKV_H
+#define LRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LRKV_OK = 0,
+    LRKV_ERR_INVALID_ARG = -1,   /* null pointer, bad size or shape                  */
+    LRKV_ERR_UNSUPPORTED = -2,   /* valid but not compiled: rank / head_dim / groups */
+    LRKV_ERR_CAPACITY = -3,      /* the append would overflow the cache              */
+    LRKV_ERR_WORKSPACE = -4,     /* workspace missing or too small                   */
+    LRKV_ERR_HIP = -5            /* a HIP call failed                                */
+} lrkv_status;
+
+typedef enum {
+    LRKV_FMT_FP16 = 0,           /* latents stored as fp16                            */
+    LRKV_FMT_INT4_G32 = 1        /* symmetric int4 codes, one fp16 scale per 32 dims  */
+} lrkv_fmt;
+
+typedef enum {
+    LRKV_MODE_ROPE_RECON = 0,    /* rebuild K = H^k B^k per tile, RoPE, attend        */
+    LRKV_MODE_ABSORBED = 1,      /* no RoPE: scores = H^k q', q' given by the caller  */
+    LRKV_MODE_HYBRID_PAGED = 2   /* dense + factored pages (PuzzleKV)                 */
+} lrkv_mode;
+
+/* Tokens per cache block of the value layout and per attention tile. */
+#define LRKV_BLOCK 32
+
+/*
+ * Latent cache (Palu modes). Query head j (of Hq = units * s * g_q) reads KV
+ * head k = j / g_q, which is column block (k % s) of unit k / s.
+ *
+ * Layouts (all device memory, caller-owned, `capacity` a multiple of 32):
+ *   fp16:  hk  [batch][units][capacity][rank]               half, token-major
+ *          hv  [batch][units][capacity/32][rank][32]        half, each 32-token
+ *                                                          block stored dim-major
+ *   int4:  hk  [batch][units][capacity][rank/2]             uint8; dims 2i and 2i+1
+ *                                                          in the low / high nibble
+ *          sk  [batch][units][capacity][rank/32]            half scales
+ *          hv  [batch][units][capacity/32][rank][16]        uint8; within a block,
+ *                                                          tokens 2i and 2i+1 of one
+ *                                                          dim in the low / high nibble
+ *          sv  [batch][units][capacity/32][rank/32][32]     half scales, token-minor
+ *   Codes are 4-bit two's complement in [-7, 7]; value = code * scale.
+ */
+typedef struct lrkv_latent_cache {
+    int32_t batch;        /* B                                                  */
+    int32_t units;        /* U: G-LRD groups, or KV heads when kv_per_unit = 1  */
+    int32_t kv_per_unit;  /* s: KV heads rebuilt from one unit's latents        */
+    int32_t q_per_kv;     /* g_q: query heads per KV head (GQA)                 */
+    int32_t head_dim;     /* d_h                                                */
+    int32_t rank;         /* r: latent width per unit                           */
+    int32_t capacity;     /* tokens per sequence (multiple of 32)               */
+    int32_t fmt;          /* lrkv_fmt                                           */
+    float rope_theta;     /* RoPE base; 0 disables RoPE                         */
+    void *hk, *hv;        /* key / value latents (layouts above)                */
+    void *sk, *sv;        /* int4 scales; NULL for fp16                         */
+    int32_t *lens;        /* device int32 [batch]                               */
+} lrkv_latent_cache;
+
+/*
+ * Hybrid paged cache (PuzzleKV). Page p of a sequence holds tokens
+ * [p*P, (p+1)*P). page_table[b][h][p] >= 0: the page is factored and its
+ * factors sit at that slot of lk/rk/lv/rv; < 0: the page is dense and sits in
+ * dense slot (-1 - entry); LRKV_PAGE_EMPTY: not written yet. Dense slots: sink
+ * page p < sink_pages uses slot p; any other dense page uses slot
+ * sink_pages + (p - sink_pages) % window_pages.
+ *
+ *   dense_k, dense_v [batch][kv_heads][sink_pages+window_pages][P][head_dim] half
+ *   lk, lv           [batch][kv_heads][max_pages][P][rank]                  half
+ *   rk, rv           [batch][kv_heads][max_pages][rank][head_dim]           half
+ *   page_table       [batch][kv_heads][max_pages]                           int32
+ */
+#define LRKV_PAGE_EMPTY ((int32_t)0x80000000)
+
+typedef struct lrkv_paged_cache {
+    int32_t batch, kv_heads, q_per_kv, head_dim;
+    int32_t page_size;    /* P                                                  */
+    int32_t sink_pages, window_pages;
+    int32_t rank_k, rank_v;
+    int32_t max_pages;    /* pages per sequence (capacity = max_pages * P)      */
+    void *dense_k, *dense_v;
+    void *lk, *rk, *lv, *rv;
+    int32_t *page_table;  /* device                                             */
+    int32_t *lens;        /* device int32 [batch]                               */
+} lrkv_paged_cache;
+
+/* Human-readable name of a status code (static string). */
+const char *lrkv_status_string(int32_t status);
+
+/* ABI version (major * 100 + minor). */
+int32_t lrkv_version(void);
+
+/*
+ * Bytes of workspace lrkv_decode_attn needs for this cache, length bound and
+ * split count (n_split <= 0 picks the library's default). Returns 0 when the
+ * arguments are invalid. `cache` points to an lrkv_latent_cache for the Palu
+ * modes and to an lrkv_paged_cache for LRKV_MODE_HYBRID_PAGED.
+ */
+size_t lrkv_decode_workspace_bytes(int32_t mode, const void *cache, int32_t host_max_len,
+                                   int32_t n_split);
+
+/*
+ * Append n_new tokens to every sequence: token i of sequence b is written at
+ * position lens[b] + i, then lens[b] += n_new.
+ *
+ * Palu modes (cache = lrkv_latent_cache*): new_k, new_v are device float32
+ * [batch][units][n_new][rank] latents h = x A (in the Hadamard-mixed basis for
+ * int4 caches). fp16 caches store round-to-nearest-even fp16. int4 caches
+ * quantise each token's 32-element groups: s = fp16_rne(fp32(amax) / 7)
+ * (+inf saturates to 65504), code = clamp(round_half_even(x / s), -7, 7) with
+ * the quotient formed in fp64; s == 0 gives zero codes.
+ *
+ * Hybrid mode (cache = lrkv_paged_cache*): new_k, new_v are device fp16
+ * [batch][kv_heads][n_new][head_dim]. A token is written to its page's dense
+ * slot unless the page is already factored (then it is skipped: prefill
+ * factors those pages from the caller's buffer first). Before a token reuses a
+ * window slot, the page that owned it must have been factored
+ * (lrkv_factor_page); the first token of a page records the dense slot in the
+ * page table.
+ *
+ * Errors: INVALID_ARG (null pointers, n_new < 1, bad shapes), UNSUPPORTED
+ * (rank not a multiple of 32 for int4, unsupported sizes), CAPACITY
+ * (host_max_len + n_new exceeds the capacity).
+ */
+int32_t lrkv_append_latent(int32_t mode, const void *cache, const void *new_k, const void *new_v,
+                           int32_t n_new, int32_t host_max_len, void *stream);
+
+/*
+ * Single-query decode attention for every sequence and query head.
+ *
+ * LRKV_MODE_ROPE_RECON: q device float32 [batch][Hq][head_dim], un-rotated;
+ *   bk device fp16 [units][rank][kv_per_unit*head_dim] (B^k, or the
+ *   Hadamard-mixed R^T B^k for int4 caches); q_pos device int32 [batch] query
+ *   positions (NULL: lens[b] - 1). Keys of token t are rotated at position t,
+ *   the query at q_pos. out: device float32 [batch][Hq][rank], o = p H^v.
+ * LRKV_MODE_ABSORBED: q device float32 [batch][Hq][rank] absorbed queries
+ *   q' = q (B^k)^T; bk and q_pos must be NULL; rope_theta is ignored.
+ *   out: float32 [batch][Hq][rank].
+ * LRKV_MODE_HYBRID_PAGED: q device float32 [batch][Hq][head_dim]; bk, q_pos
+ *   NULL; out float32 [batch][Hq][head_dim].
+ *
+ * sm_scale: softmax scale (<= 0 selects 1/sqrt(head_dim)). n_split: number of
+ * sequence chunks attended in parallel and merged by online softmax (<= 0:
+ * library default); the result does not depend on it beyond rounding.
+ * Every lens[b] must be >= 1.
+ *
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (ws_bytes smaller than
+ * lrkv_decode_workspace_bytes for the same arguments).
+ */
+int32_t lrkv_decode_attn(int32_t mode, const void *cache, const float *q, const void *bk,
+                         const int32_t *q_pos, float sm_scale, float *out, void *workspace,
+                         size_t ws_bytes, int32_t host_max_len, int32_t n_split, void *stream);
+
+/*
+ * Factor pages of a hybrid cache: for each (b, kv_head, page) triple in
+ * `pages` (device int32 [n_pages][3]) and for K and V separately, form the
+ * Gram matrix G = X X^T of the P x head_dim page X, take its top-r eigenvectors
+ * Q_r (cyclic Jacobi in fp32, at most max_sweeps sweeps, <= 0: 15), store
+ * L = Q_r and R = Q_r^T X as fp16 in factor slot `page`, and set the page-table
+ * entry to `page`.
+ *
+ * src_k / src_v NULL: X is read from the page's dense slot (decode path; a
+ * triple whose entry is not dense is skipped). Otherwise X is read from the
+ * caller's device fp16 [batch][kv_heads][src_len][head_dim] buffers (prefill
+ * path; the page must satisfy (page+1)*P <= src_len). Triples out of range are
+ * skipped.
+ *
+ * Errors: INVALID_ARG (null cache/pages, n_pages < 0, bad shapes),
+ * UNSUPPORTED (page_size != 32 or ranks outside 1..32).
+ */
+int32_t lrkv_factor_page(const lrkv_paged_cache *cache, const int32_t *pages, int32_t n_pages,
+                         const void *src_k, const void *src_v, int32_t src_len,
+                         int32_t max_sweeps, void *stream);
+
+/*
+ * Host-side planner for the hybrid cache (no device access, no launch): list
+ * the (b, kv_head, page) triples that become factored when n_new tokens are
+ * appended to sequences whose current lengths are host_lens[0..batch) (host
+ * memory): pages p with sink_pages <= p < ceil((len + n_new) / P) -
+ * window_pages that were not already factored at length len (PuzzleKV section
+ * 3.3, step 5: a page is factored once it is full and has left the window).
+ * Writes at most max_out triples to out (host int32 [max_out][3], ordered by b,
+ * kv_head, page) and returns how many there are in total (which may exceed
+ * max_out), or a negative lrkv_status on invalid arguments.
+ *
+ * Decode (n_new = 1): factor the returned pages (src NULL) before appending.
+ * Prefill (every len = 0): factor them from the caller's dense buffer, then
+ * append all tokens; the append skips tokens of factored pages.
+ */
+int32_t lrkv_paged_plan(const lrkv_paged_cache *cache, const int32_t *host_lens, int32_t n_new,
+                        int32_t *out, int32_t max_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRKV_H */

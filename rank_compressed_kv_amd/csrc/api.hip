@@ -1,0 +1,250 @@
+// C ABI of liblrkv.so: host-side validation, workspace sizing and dispatch.
+// Every check runs before anything is enqueued; a failing call touches no
+// device memory. The library allocates nothing.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace lrkv {
+
+bool latent_shape_supported(int mode, const LatentGeom& g);
+
+LatentGeom latent_geom(const lrkv_latent_cache* c) {
+    LatentGeom g;
+    g.B = c->batch;
+    g.U = c->units;
+    g.s = c->kv_per_unit;
+    g.gq = c->q_per_kv;
+    g.dh = c->head_dim;
+    g.r = c->rank;
+    g.cap = c->capacity;
+    g.fmt = c->fmt;
+    g.theta = c->rope_theta;
+    g.Hq = c->units * c->kv_per_unit * c->q_per_kv;
+    return g;
+}
+
+// Chunking of the sequence: enough workgroups to cover the 256 compute units
+// a couple of times, chunks a multiple of the 32-token tile.
+static void pick_split(int per_split_groups, int host_max_len, int n_split, int target,
+                       int* out_split, int* out_chunk) {
+    const int tiles = (host_max_len + kTile - 1) / kTile;
+    if (n_split <= 0) {
+        n_split = (target + per_split_groups - 1) / per_split_groups;
+    }
+    if (n_split > tiles) n_split = tiles;
+    if (n_split < 1) n_split = 1;
+    const int chunk_tiles = (tiles + n_split - 1) / n_split;
+    *out_chunk = chunk_tiles * kTile;
+    *out_split = (tiles + chunk_tiles - 1) / chunk_tiles;
+}
+
+LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len, int n_split) {
+    LatentWorkspace w;
+    const int target = mode == LRKV_MODE_ROPE_RECON ? 512 : 1024;
+    pick_split(g.B * g.U, host_max_len, n_split, target, &w.n_split, &w.chunk);
+    size_t off = 0;
+    w.part_off = off;
+    off += align_up((size_t)g.B * g.Hq * w.n_split * (g.r + 2) * sizeof(float), 256);
+    w.qp_off = off;
+    w.qs_off = off;
+    if (mode == LRKV_MODE_ROPE_RECON) {
+        off += align_up((size_t)g.B * g.Hq * g.dh * g.r * sizeof(half_t), 256);
+        w.qs_off = off;
+        off += align_up((size_t)g.B * g.Hq * sizeof(float), 256);
+    }
+    w.total = off;
+    return w;
+}
+
+PagedWorkspace paged_workspace(const lrkv_paged_cache* c, int host_max_len, int n_split) {
+    PagedWorkspace w;
+    const int npg = (host_max_len + c->page_size - 1) / c->page_size;
+    const int groups = c->batch * c->kv_heads;
+    if (n_split <= 0) n_split = (2048 + groups - 1) / groups;
+    if (n_split > npg) n_split = npg;
+    if (n_split < 1) n_split = 1;
+    w.pages_per_split = (npg + n_split - 1) / n_split;
+    if (w.pages_per_split < 1) w.pages_per_split = 1;
+    w.n_split = (npg + w.pages_per_split - 1) / w.pages_per_split;
+    if (w.n_split < 1) w.n_split = 1;
+    w.part_off = 0;
+    w.total = align_up((size_t)c->batch * c->kv_heads * c->q_per_kv * w.n_split *
+                           (c->head_dim + 2) * sizeof(float), 256);
+    return w;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int32_t check_latent(const lrkv_latent_cache* c) {
+    if (!c) return LRKV_ERR_INVALID_ARG;
+    if (c->batch < 1 || c->units < 1 || c->kv_per_unit < 1 || c->q_per_kv < 1 ||
+        c->head_dim < 2 || (c->head_dim & 1) || c->rank < 8 || (c->rank % 8) ||
+        c->capacity < kTile || (c->capacity % kTile))
+        return LRKV_ERR_INVALID_ARG;
+    if (c->fmt != LRKV_FMT_FP16 && c->fmt != LRKV_FMT_INT4_G32) return LRKV_ERR_INVALID_ARG;
+    if (!(c->rope_theta >= 0.0f) || !isfinite(c->rope_theta)) return LRKV_ERR_INVALID_ARG;
+    if (!c->hk || !c->hv || !c->lens) return LRKV_ERR_INVALID_ARG;
+    if (!aligned16(c->hk) || !aligned16(c->hv)) return LRKV_ERR_INVALID_ARG;
+    if (c->fmt == LRKV_FMT_INT4_G32) {
+        if (!c->sk || !c->sv) return LRKV_ERR_INVALID_ARG;
+        if (c->rank % 32) return LRKV_ERR_UNSUPPORTED;
+    }
+    if ((long)c->batch * c->units * (long)c->capacity * c->rank > (1L << 40)) return LRKV_ERR_INVALID_ARG;
+    return LRKV_OK;
+}
+
+static int32_t check_paged(const lrkv_paged_cache* c) {
+    if (!c) return LRKV_ERR_INVALID_ARG;
+    if (c->batch < 1 || c->kv_heads < 1 || c->q_per_kv < 1 || c->head_dim < 8 ||
+        c->page_size < 1 || c->sink_pages < 0 || c->window_pages < 1 || c->rank_k < 1 ||
+        c->rank_v < 1 || c->max_pages < 1)
+        return LRKV_ERR_INVALID_ARG;
+    if (!c->dense_k || !c->dense_v || !c->lk || !c->rk || !c->lv || !c->rv || !c->page_table ||
+        !c->lens)
+        return LRKV_ERR_INVALID_ARG;
+    if (c->head_dim != 128 || c->page_size != 32 || c->q_per_kv > 4 || c->rank_k > 32 ||
+        c->rank_v > 32)
+        return LRKV_ERR_UNSUPPORTED;
+    if (!aligned16(c->dense_k) || !aligned16(c->dense_v) || !aligned16(c->rk) || !aligned16(c->rv))
+        return LRKV_ERR_INVALID_ARG;
+    return LRKV_OK;
+}
+
+}  // namespace lrkv
+
+using namespace lrkv;
+
+extern "C" {
+
+const char* lrkv_status_string(int32_t s) {
+    switch (s) {
+        case LRKV_OK: return "ok";
+        case LRKV_ERR_INVALID_ARG: return "invalid argument";
+        case LRKV_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case LRKV_ERR_CAPACITY: return "cache capacity exceeded";
+        case LRKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case LRKV_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int32_t lrkv_version(void) { return 100; }
+
+size_t lrkv_decode_workspace_bytes(int32_t mode, const void* cache, int32_t host_max_len,
+                                   int32_t n_split) {
+    if (host_max_len < 1) return 0;
+    if (mode == LRKV_MODE_HYBRID_PAGED) {
+        const lrkv_paged_cache* c = (const lrkv_paged_cache*)cache;
+        if (check_paged(c) != LRKV_OK) return 0;
+        if (host_max_len > c->max_pages * c->page_size) return 0;
+        return paged_workspace(c, host_max_len, n_split).total;
+    }
+    if (mode != LRKV_MODE_ROPE_RECON && mode != LRKV_MODE_ABSORBED) return 0;
+    const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
+    if (check_latent(c) != LRKV_OK) return 0;
+    if (host_max_len > c->capacity) return 0;
+    return latent_workspace(mode, latent_geom(c), host_max_len, n_split).total;
+}
+
+int32_t lrkv_append_latent(int32_t mode, const void* cache, const void* new_k, const void* new_v,
+                           int32_t n_new, int32_t host_max_len, void* stream) {
+    if (!cache || !new_k || !new_v || n_new < 1 || host_max_len < 0) return LRKV_ERR_INVALID_ARG;
+    if (!aligned16(new_k) || !aligned16(new_v)) return LRKV_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (mode == LRKV_MODE_HYBRID_PAGED) {
+        const lrkv_paged_cache* c = (const lrkv_paged_cache*)cache;
+        int32_t rc = check_paged(c);
+        if (rc != LRKV_OK) return rc;
+        if ((long)host_max_len + n_new > (long)c->max_pages * c->page_size) return LRKV_ERR_CAPACITY;
+        return launch_append_paged(c, (const half_t*)new_k, (const half_t*)new_v, n_new, st);
+    }
+    if (mode != LRKV_MODE_ROPE_RECON && mode != LRKV_MODE_ABSORBED) return LRKV_ERR_INVALID_ARG;
+    const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
+    int32_t rc = check_latent(c);
+    if (rc != LRKV_OK) return rc;
+    if ((long)host_max_len + n_new > c->capacity) return LRKV_ERR_CAPACITY;
+    return launch_append_latent(c, (const float*)new_k, (const float*)new_v, n_new, st);
+}
+
+int32_t lrkv_decode_attn(int32_t mode, const void* cache, const float* q, const void* bk,
+                         const int32_t* q_pos, float sm_scale, float* out, void* workspace,
+                         size_t ws_bytes, int32_t host_max_len, int32_t n_split, void* stream) {
+    if (!cache || !q || !out || host_max_len < 1) return LRKV_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (mode == LRKV_MODE_HYBRID_PAGED) {
+        const lrkv_paged_cache* c = (const lrkv_paged_cache*)cache;
+        int32_t rc = check_paged(c);
+        if (rc != LRKV_OK) return rc;
+        if (bk || q_pos) return LRKV_ERR_INVALID_ARG;
+        if (host_max_len > c->max_pages * c->page_size) return LRKV_ERR_INVALID_ARG;
+        const PagedWorkspace w = paged_workspace(c, host_max_len, n_split);
+        if (!workspace || ws_bytes < w.total || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
+        const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
+        return launch_decode_hybrid(c, q, scale, out, workspace, w, st);
+    }
+    if (mode != LRKV_MODE_ROPE_RECON && mode != LRKV_MODE_ABSORBED) return LRKV_ERR_INVALID_ARG;
+    const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
+    int32_t rc = check_latent(c);
+    if (rc != LRKV_OK) return rc;
+    if (host_max_len > c->capacity) return LRKV_ERR_INVALID_ARG;
+    if (mode == LRKV_MODE_ROPE_RECON) {
+        if (!bk) return LRKV_ERR_INVALID_ARG;
+    } else if (bk || q_pos) {
+        return LRKV_ERR_INVALID_ARG;
+    }
+    const LatentGeom g = latent_geom(c);
+    if (g.r % 32) return LRKV_ERR_UNSUPPORTED;
+    if (!latent_shape_supported(mode, g)) return LRKV_ERR_UNSUPPORTED;
+    const LatentWorkspace w = latent_workspace(mode, g, host_max_len, n_split);
+    if (!workspace || ws_bytes < w.total || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
+    return launch_decode_latent(mode, c, q, (const half_t*)bk, q_pos, scale, out, workspace, w, st);
+}
+
+int32_t lrkv_factor_page(const lrkv_paged_cache* cache, const int32_t* pages, int32_t n_pages,
+                         const void* src_k, const void* src_v, int32_t src_len,
+                         int32_t max_sweeps, void* stream) {
+    int32_t rc = check_paged(cache);
+    if (rc != LRKV_OK) return rc;
+    if (n_pages < 0 || (n_pages > 0 && !pages)) return LRKV_ERR_INVALID_ARG;
+    if ((src_k == nullptr) != (src_v == nullptr)) return LRKV_ERR_INVALID_ARG;
+    if (src_k && (src_len < cache->page_size || !aligned16(src_k) || !aligned16(src_v)))
+        return LRKV_ERR_INVALID_ARG;
+    if (max_sweeps <= 0) max_sweeps = 15;
+    if (max_sweeps > 100) return LRKV_ERR_INVALID_ARG;
+    return launch_factor_page(cache, pages, n_pages, (const half_t*)src_k, (const half_t*)src_v,
+                              src_k ? src_len : 0, max_sweeps, (hipStream_t)stream);
+}
+
+int32_t lrkv_paged_plan(const lrkv_paged_cache* c, const int32_t* host_lens, int32_t n_new,
+                        int32_t* out, int32_t max_out) {
+    int32_t rc = check_paged(c);
+    if (rc != LRKV_OK) return rc;
+    if (!host_lens || n_new < 0 || max_out < 0 || (max_out > 0 && !out)) return LRKV_ERR_INVALID_ARG;
+    const long P = c->page_size;
+    long count = 0;
+    for (int b = 0; b < c->batch; ++b) {
+        const long len = host_lens[b];
+        if (len < 0 || len + n_new > (long)c->max_pages * P) return LRKV_ERR_INVALID_ARG;
+        // pages factored at length n: sink <= p < ceil(n / P) - window
+        const long before = (len + P - 1) / P - c->window_pages;
+        const long after = (len + n_new + P - 1) / P - c->window_pages;
+        const long lo = before > c->sink_pages ? before : c->sink_pages;
+        for (int h = 0; h < c->kv_heads; ++h) {
+            for (long p = lo; p < after; ++p) {
+                if (count < max_out) {
+                    out[3 * count + 0] = b;
+                    out[3 * count + 1] = h;
+                    out[3 * count + 2] = (int32_t)p;
+                }
+                ++count;
+            }
+        }
+    }
+    return count > 0x7fffffff ? LRKV_ERR_INVALID_ARG : (int32_t)count;
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// Cache append kernels: fp16 latents, int4 latents (group-32 symmetric codec) and
+// dense tokens of the hybrid paged cache.
+//
+// Palu digest, Method details: the cache holds per-token latents h = x A
+// instead of keys and values. PuzzleKV section 3.3, step 5: new key/value pairs
+// go to the newest dense page. The int4 rule (Shard section 5, symmetric
+// [-7, 7]; Palu digest Appendix, per-token groups of 32) is documented in lrkv.h.
+#include "common.h"
+
+namespace lrkv {
+namespace {
+
+__global__ void bump_lens(int32_t* lens, int B, int n_new) {
+    int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) lens[b] += n_new;
+}
+
+// One thread per (b, u, i, 8 consecutive dims). Keys go token-major, values into
+// the dim-major 32-token block of their position.
+__global__ void append_fp16(const float* __restrict__ nk, const float* __restrict__ nv,
+                            half_t* __restrict__ hk, half_t* __restrict__ hv,
+                            const int32_t* __restrict__ lens, int B, int U, int r, int cap,
+                            int n_new) {
+    const int r8 = r / 8;
+    const long total = (long)B * U * n_new * r8;
+    long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    const int d8 = (int)(e % r8);
+    long rest = e / r8;
+    const int i = (int)(rest % n_new);
+    rest /= n_new;
+    const int u = (int)(rest % U);
+    const int b = (int)(rest / U);
+    const int pos = lens[b] + i;
+    const long src = (((long)b * U + u) * n_new + i) * r + d8 * 8;
+    const float4 k0 = *reinterpret_cast<const float4*>(nk + src);
+    const float4 k1 = *reinterpret_cast<const float4*>(nk + src + 4);
+    const float4 v0 = *reinterpret_cast<const float4*>(nv + src);
+    const float4 v1 = *reinterpret_cast<const float4*>(nv + src + 4);
+    half8 kh;
+    kh[0] = (half_t)k0.x; kh[1] = (half_t)k0.y; kh[2] = (half_t)k0.z; kh[3] = (half_t)k0.w;
+    kh[4] = (half_t)k1.x; kh[5] = (half_t)k1.y; kh[6] = (half_t)k1.z; kh[7] = (half_t)k1.w;
+    const long bu = (long)b * U + u;
+    *reinterpret_cast<half8*>(hk + (bu * cap + pos) * r + d8 * 8) = kh;
+    const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    half_t* vblk = hv + ((bu * (cap / kTile) + pos / kTile) * r + d8 * 8) * kTile + pos % kTile;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) vblk[k * kTile] = (half_t)vv[k];
+}
+
+// The codec of one 32-element group: fp16 scale and the 32 codes.
+__device__ void quant_group(const float* __restrict__ x, int* codes, half_t* scale) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    const float s32 = amax / 7.0f;                       // IEEE fp32 division
+    half_t s16 = (half_t)s32;                            // round to nearest even
+    if (__builtin_isinf((float)s16)) s16 = (half_t)65504.0f;
+    const double den = (double)(float)s16;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        int c = 0;
+        if (den != 0.0) {
+            double qd = rint((double)x[k] / den);        // fp64 quotient, half-even
+            qd = fmin(7.0, fmax(-7.0, qd));
+            c = (int)qd;
+        }
+        codes[k] = c;
+    }
+    *scale = s16;
+}
+
+// Keys: one thread per (b, u, i, group). 16 packed bytes + one scale.
+__global__ void append_int4_k(const float* __restrict__ nk, uint8_t* __restrict__ hk,
+                              half_t* __restrict__ sk, const int32_t* __restrict__ lens, int B,
+                              int U, int r, int cap, int n_new) {
+    const int G = r / 32;
+    const long total = (long)B * U * n_new * G;
+    long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    const int g = (int)(e % G);
+    long rest = e / G;
+    const int i = (int)(rest % n_new);
+    rest /= n_new;
+    const int u = (int)(rest % U);
+    const int b = (int)(rest / U);
+    const int pos = lens[b] + i;
+    const float* x = nk + ((((long)b * U + u) * n_new + i) * r + g * 32);
+    int codes[32];
+    half_t s16;
+    quant_group(x, codes, &s16);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc |= (uint32_t)(codes[q * 8 + k] & 0xF) << (4 * k);
+        w[q] = acc;
+    }
+    const long bu = (long)b * U + u;
+    *reinterpret_cast<uint4*>(hk + (bu * cap + pos) * (r / 2) + g * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    sk[(bu * cap + pos) * G + g] = s16;
+}
+
+// Values: one thread per (b, u, token pair, group) so that no two threads share a
+// byte; a partner token outside the appended range keeps its nibble.
+__global__ void append_int4_v(const float* __restrict__ nv, uint8_t* __restrict__ hv,
+                              half_t* __restrict__ sv, const int32_t* __restrict__ lens, int B,
+                              int U, int r, int cap, int n_new) {
+    const int G = r / 32;
+    const int n_pairs = n_new / 2 + 2;       // pairs touched by [len, len + n_new)
+    const long total = (long)B * U * n_pairs * G;
+    long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    const int g = (int)(e % G);
+    long rest = e / G;
+    const int pi = (int)(rest % n_pairs);
+    rest /= n_pairs;
+    const int u = (int)(rest % U);
+    const int b = (int)(rest / U);
+    const int len = lens[b];
+    const int pair = len / 2 + pi;           // covers tokens 2*pair, 2*pair + 1
+    const long bu = (long)b * U + u;
+    int codes[2][32];
+    bool own[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int pos = 2 * pair + h;
+        own[h] = pos >= len && pos < len + n_new;
+        if (own[h]) {
+            half_t s16;
+            quant_group(nv + ((bu * n_new + (pos - len)) * r + g * 32), codes[h], &s16);
+            sv[((bu * (cap / kTile) + pos / kTile) * G + g) * kTile + pos % kTile] = s16;
+        }
+    }
+    if (!own[0] && !own[1]) return;
+    const int pos0 = 2 * pair;
+    uint8_t* base = hv + ((bu * (cap / kTile) + pos0 / kTile) * r + g * 32) * (kTile / 2) + (pos0 % kTile) / 2;
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+        uint8_t* p = base + k * (kTile / 2);
+        uint32_t byte = own[0] && own[1] ? 0u : (uint32_t)*p;
+        if (own[0]) byte = (byte & 0xF0u) | ((uint32_t)codes[0][k] & 0xFu);
+        if (own[1]) byte = (byte & 0x0Fu) | (((uint32_t)codes[1][k] & 0xFu) << 4);
+        *p = (uint8_t)byte;
+    }
+}
+
+// Hybrid cache: one thread per (b, h, i, 8 dims) copying K and V into the dense
+// slot of the token's page, unless that page is already factored.
+__global__ void append_paged(const half_t* __restrict__ nk, const half_t* __restrict__ nv,
+                             half_t* __restrict__ dk, half_t* __restrict__ dv,
+                             int32_t* __restrict__ table, const int32_t* __restrict__ lens, int B,
+                             int H, int d, int P, int sink, int window, int max_pages, int n_new) {
+    const int d8 = d / 8;
+    const long total = (long)B * H * n_new * d8;
+    long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    const int c8 = (int)(e % d8);
+    long rest = e / d8;
+    const int i = (int)(rest % n_new);
+    rest /= n_new;
+    const int h = (int)(rest % H);
+    const int b = (int)(rest / H);
+    const int pos = lens[b] + i;
+    const int p = pos / P;
+    const long bh = (long)b * H + h;
+    int32_t* entry = table + bh * max_pages + p;
+    if (*entry >= 0) return;                 // factored already (prefill)
+    const int slot = p < sink ? p : sink + (p - sink) % window;
+    const long src = (bh * n_new + i) * d + c8 * 8;
+    const long dst = ((bh * (sink + window) + slot) * P + pos % P) * d + c8 * 8;
+    *reinterpret_cast<half8*>(dk + dst) = *reinterpret_cast<const half8*>(nk + src);
+    *reinterpret_cast<half8*>(dv + dst) = *reinterpret_cast<const half8*>(nv + src);
+    if (pos % P == 0 && c8 == 0) *entry = -1 - slot;
+}
+
+inline unsigned blocks_for(long n, int bs) { return (unsigned)((n + bs - 1) / bs); }
+
+}  // namespace
+
+int32_t launch_append_latent(const lrkv_latent_cache* c, const float* nk, const float* nv,
+                             int n_new, hipStream_t st) {
+    const int B = c->batch, U = c->units, r = c->rank, cap = c->capacity;
+    if (c->fmt == LRKV_FMT_FP16) {
+        const long n = (long)B * U * n_new * (r / 8);
+        hipLaunchKernelGGL(append_fp16, dim3(blocks_for(n, 256)), dim3(256), 0, st, nk, nv,
+                           (half_t*)c->hk, (half_t*)c->hv, c->lens, B, U, r, cap, n_new);
+    } else {
+        const long nk_threads = (long)B * U * n_new * (r / 32);
+        hipLaunchKernelGGL(append_int4_k, dim3(blocks_for(nk_threads, 128)), dim3(128), 0, st, nk,
+                           (uint8_t*)c->hk, (half_t*)c->sk, c->lens, B, U, r, cap, n_new);
+        const long nv_threads = (long)B * U * (n_new / 2 + 2) * (r / 32);
+        hipLaunchKernelGGL(append_int4_v, dim3(blocks_for(nv_threads, 128)), dim3(128), 0, st, nv,
+                           (uint8_t*)c->hv, (half_t*)c->sv, c->lens, B, U, r, cap, n_new);
+    }
+    hipLaunchKernelGGL(bump_lens, dim3(blocks_for(B, 64)), dim3(64), 0, st, c->lens, B, n_new);
+    return last_launch_status();
+}
+
+int32_t launch_append_paged(const lrkv_paged_cache* c, const half_t* nk, const half_t* nv,
+                            int n_new, hipStream_t st) {
+    const int B = c->batch, H = c->kv_heads, d = c->head_dim;
+    const long n = (long)B * H * n_new * (d / 8);
+    hipLaunchKernelGGL(append_paged, dim3(blocks_for(n, 256)), dim3(256), 0, st, nk, nv,
+                       (half_t*)c->dense_k, (half_t*)c->dense_v, c->page_table, c->lens, B, H, d,
+                       c->page_size, c->sink_pages, c->window_pages, c->max_pages, n_new);
+    hipLaunchKernelGGL(bump_lens, dim3(blocks_for(B, 64)), dim3(64), 0, st, c->lens, B, n_new);
+    return last_launch_status();
+}
+
+}  // namespace lrkv

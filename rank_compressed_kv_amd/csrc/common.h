@@ -1,0 +1,101 @@
+// Internal definitions shared by the lrkv HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lrkv.h"
+
+namespace lrkv {
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kTile = 32;          // tokens per attention tile == cache block
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- MFMA wrappers
+// v_mfma_f32_32x32x16_f16. Lane l supplies A[l%32][8*(l/32) + 0..7] and
+// B[8*(l/32) + 0..7][l%32]; accumulator element i of lane l is
+// D[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x32_f16. Lane l supplies A[l%16][8*(l/16) + 0..7] and
+// B[8*(l/16) + 0..7][l%16]; accumulator element i of lane l is
+// D[4*(l/16) + i][l%16].
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- lane helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <int W>
+__device__ __forceinline__ float reduce_max_width(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+template <int W>
+__device__ __forceinline__ float reduce_sum_width(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Sign-extended 4-bit code in nibble `k` (0..7) of a 32-bit word.
+__device__ __forceinline__ int nibble(uint32_t w, int k) {
+    return ((int)(w << (28 - 4 * k))) >> 28;
+}
+
+// ---------------------------------------------------------------- launch plumbing
+struct Status {
+    static int32_t from_hip(hipError_t e) { return e == hipSuccess ? LRKV_OK : LRKV_ERR_HIP; }
+};
+
+inline int32_t last_launch_status() { return Status::from_hip(hipGetLastError()); }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- kernel entry points (host side)
+struct LatentGeom {
+    int B, U, s, gq, dh, r, cap, fmt, Hq;
+    float theta;
+};
+
+LatentGeom latent_geom(const lrkv_latent_cache* c);
+
+// Decode workspace for the Palu modes: partials [B][Hq][n_split][r + 2] float,
+// then (RoPE mode) the rotated-basis queries [B][Hq][dh][r] half and their
+// scales [B][Hq] float.
+struct LatentWorkspace {
+    size_t part_off, qp_off, qs_off, total;
+    int n_split, chunk;
+};
+LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len, int n_split);
+
+int32_t launch_append_latent(const lrkv_latent_cache* c, const float* nk, const float* nv,
+                             int n_new, hipStream_t st);
+int32_t launch_append_paged(const lrkv_paged_cache* c, const half_t* nk, const half_t* nv,
+                            int n_new, hipStream_t st);
+int32_t launch_decode_latent(int mode, const lrkv_latent_cache* c, const float* q,
+                             const half_t* bk, const int32_t* q_pos, float sm_scale, float* out,
+                             void* ws, const LatentWorkspace& w, hipStream_t st);
+
+struct PagedWorkspace {
+    size_t part_off, total;
+    int n_split, pages_per_split;
+};
+PagedWorkspace paged_workspace(const lrkv_paged_cache* c, int host_max_len, int n_split);
+int32_t launch_decode_hybrid(const lrkv_paged_cache* c, const float* q, float sm_scale, float* out,
+                             void* ws, const PagedWorkspace& w, hipStream_t st);
+int32_t launch_factor_page(const lrkv_paged_cache* c, const int32_t* pages, int n_pages,
+                           const half_t* src_k, const half_t* src_v, int src_len, int max_sweeps,
+                           hipStream_t st);
+
+}  // namespace lrkv

@@ -1,0 +1,244 @@
+"""GPU parity of the Palu latent-cache path (append, RoPE reconstruction, absorbed
+query, split merge) against the float64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attn as oattn
+from oracle import codec as ocodec
+from tests.gpu_util import (hk_int4_codes, hv_fp16_tokens, hv_int4_codes, rel_l2, say, sv_tokens,
+                            to_dev)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3      # rel-L2 per (sequence, head) on attention outputs
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_compressed_kv_amd as R
+    R.load_library()
+
+
+def _R():
+    import rank_compressed_kv_amd as R
+    return R
+
+
+# shapes: name -> (B, U, s, g_q, d_h, r, theta, tau)
+SHAPES = {
+    "tiny_glrd": (1, 2, 2, 1, 64, 32, 1e4, 24.0),
+    "llama2_glrd": (1, 8, 4, 1, 128, 256, 1e4, 96.0),
+    "llama3_gqa": (2, 8, 1, 4, 128, 64, 5e5, 32.0),
+}
+
+
+def _make(name, T, cap, fmt, seed, q_scale=1.0, ragged=(), theta=None, mixed=False):
+    R = _R()
+    B, U, s, gq, dh, r, th, tau = SHAPES[name]
+    th = th if theta is None else theta
+    lay = synth.latent_layer(seed, B, U, T, r, s * dh, tau)
+    hk, hv, Bk = lay["hk"], lay["hv"], lay["Bk"]
+    if mixed:
+        hk, Bk = synth.hadamard_mixed(hk, Bk)
+        hv, _ = synth.hadamard_mixed(hv, lay["Bv"])
+    q = synth.queries(seed + 1000, B, U * s * gq, dh, q_scale)
+    cache = R.LatentCache(B, U, s, gq, dh, r, cap, fmt, th)
+    cache.append(to_dev(hk), to_dev(hv))
+    lens = np.full(B, T, np.int64)
+    for b, cut in enumerate(ragged[:B]):
+        lens[b] = T - cut
+    if len(ragged):
+        cache.lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        cache.host_lens[:] = lens
+    store = oattn.stored_fp16 if fmt == R.FMT_FP16 else oattn.stored_int4
+    return dict(cache=cache, hk=hk, hv=hv, Bk=Bk, q=q, lens=lens, s=s, gq=gq, dh=dh, r=r, theta=th,
+                sk=store(hk), sv=store(hv))
+
+
+def _oracle_rope(c, q_pos=None):
+    return oattn.palu_decode(c["sk"], c["sv"], c["Bk"].astype(np.float64), c["q"], c["lens"], c["s"],
+                             c["gq"], c["dh"], c["theta"], q_pos=q_pos)
+
+
+def _gpu_rope(c, n_split=0, q_pos=None):
+    R = _R()
+    qp = None if q_pos is None else to_dev(np.asarray(q_pos, np.int32))
+    out = c["cache"].decode(R.MODE_ROPE_RECON, to_dev(c["q"]), to_dev(c["Bk"]), qp, n_split=n_split)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- append
+
+def test_append_fp16_bitexact():
+    R = _R()
+    say("append fp16: B=2 U=3 r=64, appends of 37, 1, 26 tokens")
+    rng = np.random.default_rng(11)
+    cache = R.LatentCache(2, 3, 1, 1, 64, 64, 128, R.FMT_FP16, 0.0)
+    chunks = []
+    for n in (37, 1, 26):
+        a = (rng.standard_normal((2, 3, n, 64)) * 3).astype(np.float32)
+        a[0, 0, 0, :4] = [65519.0, 65520.0, 1e-8, -2.0 ** -25]     # overflow / subnormal edges
+        v = (rng.standard_normal((2, 3, n, 64))).astype(np.float32)
+        cache.append(to_dev(a), to_dev(v))
+        chunks.append((a, v))
+    torch.cuda.synchronize()
+    k_all = np.concatenate([c[0] for c in chunks], axis=2)
+    v_all = np.concatenate([c[1] for c in chunks], axis=2)
+    with np.errstate(over="ignore"):
+        ek, ev = k_all.astype(np.float16), v_all.astype(np.float16)
+    got_k = cache.hk.cpu().numpy()[:, :, :64]
+    got_v = hv_fp16_tokens(cache.hv)[:, :, :64]
+    assert np.array_equal(got_k.view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(got_v.view(np.uint16), ev.view(np.uint16))
+    assert cache.lens.cpu().tolist() == [64, 64]
+
+
+def test_append_int4_bitexact():
+    R = _R()
+    say("append int4: B=2 U=2 r=64, appends of 5, 1, 26, 1 tokens (odd offsets)")
+    rng = np.random.default_rng(12)
+    cache = R.LatentCache(2, 2, 1, 4, 128, 64, 64, R.FMT_INT4_G32, 5e5)
+    ks, vs = [], []
+    for n in (5, 1, 26, 1):
+        k = (rng.standard_normal((2, 2, n, 64)) * rng.uniform(0.01, 20)).astype(np.float32)
+        v = (rng.standard_normal((2, 2, n, 64)) * rng.uniform(0.01, 20)).astype(np.float32)
+        k[0, 0, 0, :32] = 0.0                                          # all-zero group
+        k[0, 1, 0, :32] = 0.0
+        k[0, 1, 0, 7] = -3.0                                           # single nonzero
+        k[1, 0, 0, :32] = np.float32(1.0) * np.array([7.0] + [2.5, 3.5, -2.5, 0.5] * 7 + [1.5, 6.5, -6.5], np.float32)
+        v[1, 1, 0, 32:] = np.array([7.0] + [(k + 0.5) for k in range(-4, 3)] * 4 + [0.5, 1.5, -0.5], np.float32)
+        cache.append(to_dev(k), to_dev(v))
+        ks.append(k)
+        vs.append(v)
+    torch.cuda.synchronize()
+    K = np.concatenate(ks, axis=2)
+    V = np.concatenate(vs, axis=2)
+    T = K.shape[2]
+    ck, sk = ocodec.quantize(K)
+    cv, sv = ocodec.quantize(V)
+    assert np.array_equal(hk_int4_codes(cache.hk)[:, :, :T], ck)
+    assert np.array_equal(cache.sk.cpu().numpy()[:, :, :T].view(np.uint16), sk.view(np.uint16))
+    assert np.array_equal(hv_int4_codes(cache.hv)[:, :, :T], cv)
+    assert np.array_equal(sv_tokens(cache.sv)[:, :, :T].view(np.uint16), sv.view(np.uint16))
+    # packed bytes themselves: dims 2i / 2i+1 in the low / high nibble
+    assert np.array_equal(cache.hk.cpu().numpy()[:, :, :T], ocodec.pack(ck))
+
+
+# ----------------------------------------------------------------------------- RoPE path
+
+@pytest.mark.parametrize("name,T,cap,ragged,q_scale", [
+    ("tiny_glrd", 256, 256, (), 1.0),
+    ("tiny_glrd", 200, 256, (), 6.0),
+    ("llama2_glrd", 2048, 2048, (), 1.0),
+    ("llama2_glrd", 1000, 1024, (), 8.0),
+    ("llama3_gqa", 1111, 1152, (0, 333), 1.0),
+])
+def test_rope_fp16_parity(name, T, cap, ragged, q_scale):
+    R = _R()
+    say(f"rope fp16 parity: {name} T={T} ragged={ragged} q_scale={q_scale}")
+    c = _make(name, T, cap, R.FMT_FP16, seed=21, q_scale=q_scale, ragged=ragged)
+    got = _gpu_rope(c)
+    ref = _oracle_rope(c)
+    err = rel_l2(got, ref)
+    assert err.max() <= TOL, err.max()
+
+
+@pytest.mark.parametrize("name,T,cap,ragged", [
+    ("llama3_gqa", 1500, 1536, (0, 77)),
+    ("llama2_glrd", 700, 704, ()),
+])
+def test_rope_int4_parity(name, T, cap, ragged):
+    R = _R()
+    say(f"rope int4 parity: {name} T={T} ragged={ragged}")
+    c = _make(name, T, cap, R.FMT_INT4_G32, seed=22, ragged=ragged, mixed=True)
+    err = rel_l2(_gpu_rope(c), _oracle_rope(c))
+    assert err.max() <= TOL, err.max()
+
+
+def test_rope_split_independence():
+    R = _R()
+    say("rope split independence: llama2_glrd T=1500, n_split 1/3/7/auto")
+    c = _make("llama2_glrd", 1500, 1504, R.FMT_FP16, seed=23, q_scale=4.0)
+    ref = _oracle_rope(c)
+    outs = [_gpu_rope(c, n_split=n) for n in (1, 3, 7, 0)]
+    # p enters the value MFMA as fp16 relative to each chunk's own maximum, so two
+    # chunkings differ by at most two fp16 roundings of p (unit roundoff 2^-11)
+    for o in outs:
+        assert rel_l2(o, ref).max() <= TOL
+        assert rel_l2(o, outs[0]).max() <= 2 * 2.0 ** -11
+
+
+def test_rope_query_position():
+    R = _R()
+    say("rope explicit q_pos: tiny_glrd T=256")
+    c = _make("tiny_glrd", 256, 256, R.FMT_FP16, seed=24)
+    a = _gpu_rope(c, q_pos=[255])
+    assert rel_l2(a, _gpu_rope(c)).max() <= 1e-6
+    b = _gpu_rope(c, q_pos=[17])
+    assert rel_l2(b, _oracle_rope(c, q_pos=[17])).max() <= TOL
+
+
+def test_rope_off_equals_absorbed():
+    """theta = 0: reconstruct path == absorbed path with q' = q (B^k)^T."""
+    R = _R()
+    say("rope theta=0 vs absorbed: llama2_glrd T=900")
+    c = _make("llama2_glrd", 900, 928, R.FMT_FP16, seed=25, theta=0.0)
+    got_r = _gpu_rope(c)
+    B, U, s, dh = 1, 8, 4, 128
+    Bk = c["Bk"].astype(np.float64)
+    qa = np.stack([[c["q"][b, j] @ Bk[j // s][:, (j % s) * dh:(j % s + 1) * dh].T for j in range(32)]
+                   for b in range(B)]).astype(np.float32)
+    got_a = c["cache"].decode(R.MODE_ABSORBED, to_dev(qa), sm_scale=1 / np.sqrt(dh))
+    torch.cuda.synchronize()
+    got_a = got_a.cpu().numpy()
+    ref = _oracle_rope(c)
+    assert rel_l2(got_r, ref).max() <= TOL
+    assert rel_l2(got_a, ref).max() <= TOL
+
+
+# ----------------------------------------------------------------------------- absorbed path
+
+@pytest.mark.parametrize("fmt_name,B,T,cap", [("fp16", 3, 700, 704), ("fp16", 2, 4096, 4096), ("int4", 2, 999, 1024)])
+def test_absorbed_parity(fmt_name, B, T, cap):
+    R = _R()
+    fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
+    say(f"absorbed parity: {fmt_name} B={B} T={T}")
+    U, s, r, dh = 8, 4, 256, 128
+    lay = synth.latent_layer(31, B, U, T, r, s * dh, 96.0)
+    qa = synth.queries(32, B, U * s, r, 3.0)
+    cache = R.LatentCache(B, U, s, 1, dh, r, cap, fmt, 0.0)
+    cache.append(to_dev(lay["hk"]), to_dev(lay["hv"]))
+    lens = np.array([T - 53 * b for b in range(B)])
+    cache.lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    cache.host_lens[:] = lens
+    got = cache.decode(R.MODE_ABSORBED, to_dev(qa))
+    torch.cuda.synchronize()
+    store = oattn.stored_fp16 if fmt == R.FMT_FP16 else oattn.stored_int4
+    ref = oattn.palu_decode_absorbed(store(lay["hk"]), store(lay["hv"]), qa, lens, s, 1, dh)
+    err = rel_l2(got.cpu().numpy(), ref)
+    assert err.max() <= TOL, err.max()
+
+
+# ----------------------------------------------------------------------------- full size, sampled
+
+def test_rope_full_size_sampled():
+    """Llama-2-7B-shaped G-LRD layer at T = 64K in the bench's launch configuration;
+    three query heads checked against the oracle one by one."""
+    R = _R()
+    T = 65536
+    say(f"rope full size: llama2_glrd T={T} (sampled heads 0, 13, 31)")
+    c = _make("llama2_glrd", T, T, R.FMT_FP16, seed=2)
+    got = _gpu_rope(c)
+    assert np.isfinite(got).all()
+    for j in (0, 13, 31):
+        u, w = oattn.head_unit(j, 4, 1)
+        sub = dict(c)
+        sub.update(q=c["q"][:, j:j + 1], sk=c["sk"][:, u:u + 1], sv=c["sv"][:, u:u + 1],
+                   Bk=c["Bk"][u:u + 1, :, w * 128:(w + 1) * 128], s=1, gq=1)
+        ref = _oracle_rope(sub)
+        assert rel_l2(got[:, j], ref[:, 0]).max() <= TOL
