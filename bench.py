@@ -1,0 +1,229 @@
+#!/usr/bin/env python
+"""Decode attention read directly from a low-rank latent KV cache, on one MI355X.
+
+Default workload: one Llama-2-7B-shaped attention layer on the RoPE path
+(d = 4096, 32 heads of 128, G-LRD groups of 4 heads -> 8 units, rank 256 per
+unit = 50% of the K/V width, fp16 latents), batch 1, T = 65536 cached tokens.
+
+One step = the whole decode hot path for one new token:
+  append the token's K/V latents (fp32 -> fp16 cache)            lrkv_append_latent
+  query preparation (rotated-basis queries)                      lrkv_decode_prepare
+  latent stream + on-chip reconstruction + RoPE + online
+  softmax + p.H^v, per sequence chunk                            lrkv_decode_partials
+  split-K merge                                                  lrkv_merge_partials
+Inputs are resident in HBM before the timed region. Two cache replicas are
+used in turn so that consecutive steps do not re-read the same 537 MB from the
+256 MB last-level cache.
+
+Prints one JSON line (see the repository's design doc for the fields).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "low-rank decode attn µs/step & latent-KV GB/s at T=64K; % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+# Llama-2-7B-shaped G-LRD layer
+B, U, S, GQ, DH, R, THETA, TAU = 1, 8, 4, 1, 128, 256, 1e4, 96.0
+BYTES_PER_UNIT_TOKEN = 2 * R * 2                      # K and V latents, fp16
+FLOP_PER_UNIT_TOKEN = 2 * R * S * DH + 2 * S * DH + 2 * S * R
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(T: int, budget_s: float = 12.0) -> dict:
+    """The float64 oracle timed on this host on a bounded sample of the same workload:
+    whole units (4 heads each) at full length, until the time budget is used."""
+    import synth
+    from oracle import attn as oattn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    lay = synth.latent_layer(2, 1, 1, T, R, S * DH, TAU)
+    q = synth.queries(1002, 1, S * GQ, DH)
+    hk = oattn.stored_fp16(lay["hk"])
+    hv = oattn.stored_fp16(lay["hv"])
+    Bk = lay["Bk"].astype(np.float64)
+    units, elapsed = 0, 0.0
+    while elapsed < budget_s and units < U:
+        t0 = time.perf_counter()
+        oattn.palu_decode(hk, hv, Bk, q, [T], S, GQ, DH, THETA)
+        elapsed += time.perf_counter() - t0
+        units += 1
+    gbs = units * T * BYTES_PER_UNIT_TOKEN / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{units} of {U} units (4 query heads each) at T={T}, float64 numpy oracle, "
+                      f"{elapsed:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--T", type=int, default=65536)
+    ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--n-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (reference for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the decode shards by unit, batch or sequence chunk with no exchange "
+              "except a partial-state all-gather; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rank_compressed_kv_amd as lrkv
+    import synth
+
+    lrkv.load_library()
+    dev = torch.device("cuda:0")
+    T, K, W, NR = args.T, args.steps, args.warmup, max(1, args.replicas)
+    T_init = T - 1 - W // NR
+    cap = ((T + K + W + 64) // 32) * 32
+
+    log(f"bench: generating latents for T={T_init} (B={B}, U={U}, r={R})")
+    lay = synth.latent_layer(2, B, U, T_init, R, S * DH, TAU)
+    hk0 = torch.from_numpy(lay["hk"]).to(dev)
+    hv0 = torch.from_numpy(lay["hv"]).to(dev)
+    Bk = torch.from_numpy(lay["Bk"]).to(dev)
+    del lay
+    reps = []
+    for i in range(NR):
+        c = lrkv.LatentCache(B, U, S, GQ, DH, R, cap, lrkv.FMT_FP16, THETA, device=dev)
+        c.append(hk0, hv0)
+        reps.append(c)
+    del hk0, hv0
+    step_tok = synth.latent_layer(3, B, U, W + K, R, S * DH, TAU)
+    nk = torch.from_numpy(step_tok["hk"]).to(dev)
+    nv = torch.from_numpy(step_tok["hv"]).to(dev)
+    new_k = [nk[:, :, i:i + 1].contiguous() for i in range(W + K)]
+    new_v = [nv[:, :, i:i + 1].contiguous() for i in range(W + K)]
+    q = torch.from_numpy(synth.queries(1002, B, U * S * GQ, DH)).to(dev)
+    out = torch.empty((B, U * S * GQ, R), dtype=torch.float32, device=dev)
+    for c in reps:          # the workspace must cover the longest length of the run
+        c.host_lens += K + W
+    ws = [c.workspace(lrkv.MODE_ROPE_RECON, args.n_split) for c in reps]
+    for c in reps:
+        c.host_lens -= K + W
+    torch.cuda.synchronize()
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    mode = lrkv.MODE_ROPE_RECON
+    n_ev = 5
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    lens_timed = []
+    log(f"bench: {W} warmup + {K} timed steps, {NR} cache replicas")
+    for i in range(W + K):
+        c, w = reps[i % NR], ws[i % NR]
+        timed = i >= W
+        if i == W:
+            torch.cuda.synchronize()
+            t_start.record()
+        ev = events[i - W] if timed else None
+        if timed:
+            ev[0].record()
+        c.append(new_k[i], new_v[i])
+        L = c.max_len
+        if timed:
+            ev[1].record()
+            lens_timed.append(L)
+        lrkv.decode_prepare(mode, c.desc, q, Bk, 0.0, w, L, args.n_split)
+        if timed:
+            ev[2].record()
+        lrkv.decode_partials(mode, c.desc, None, None, 0.0, w, L, args.n_split)
+        if timed:
+            ev[3].record()
+        lrkv.merge_partials(mode, c.desc, out, w, L, args.n_split)
+        if timed:
+            ev[4].record()
+    t_end.record()
+    torch.cuda.synchronize()
+
+    total_ms = t_start.elapsed_time(t_end)
+    ph = np.array([[events[k][j].elapsed_time(events[k][j + 1]) for j in range(n_ev - 1)] for k in range(K)])
+    lens_timed = np.array(lens_timed, dtype=np.float64)
+    bytes_steps = U * B * lens_timed * BYTES_PER_UNIT_TOKEN
+    flops_steps = U * B * lens_timed * FLOP_PER_UNIT_TOKEN
+    gbs = bytes_steps.sum() / (total_ms * 1e-3) / 1e9
+    part_ms = ph[:, 2].mean()
+    achieved = bytes_steps.mean() / (part_ms * 1e-3) / 1e9
+    ok = bool(np.isfinite(out.cpu().numpy()).all())
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(total_ms / K, 5),
+        "us_per_step": round(total_ms / K * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-2-7B-shaped G-LRD attention layer, RoPE reconstruct path, "
+                        "8 units x 4 heads, d_h 128, rank 256 per unit, fp16 latents",
+            "batch": B, "T": T, "T_mean_timed": float(lens_timed.mean()), "units": U,
+            "heads": U * S * GQ, "rank": R, "head_dim": DH, "rope_theta": THETA,
+            "cache_replicas": NR, "n_split": args.n_split,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "rope_decode (lrkv_decode_partials)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "detail": {
+            "phase_us": {"append": round(ph[:, 0].mean() * 1e3, 2), "prepare": round(ph[:, 1].mean() * 1e3, 2),
+                         "partials": round(ph[:, 2].mean() * 1e3, 2), "merge": round(ph[:, 3].mean() * 1e3, 2)},
+            "partials_us_p10_p50_p90": [round(float(np.percentile(ph[:, 2], p)) * 1e3, 2) for p in (10, 50, 90)],
+            "mfma_tflops_partials": round(flops_steps.mean() / (part_ms * 1e-3) / 1e12, 1),
+            "mfma_frac_partials": round(flops_steps.mean() / (part_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "bytes_per_step": float(bytes_steps.mean()),
+            "output_finite": ok,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the float64 oracle on the host (cpu_baseline)")
+        result["cpu_baseline"] = cpu_baseline(T)
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

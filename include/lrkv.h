@@ -199,6 +199,33 @@ int32_t lrkv_decode_attn(int32_t mode, const void *cache, const float *q, const 
                          size_t ws_bytes, int32_t host_max_len, int32_t n_split, void *stream);
 
 /*
+ * The three steps lrkv_decode_attn enqueues, callable one by one with the same
+ * cache, workspace, host_max_len and n_split (lrkv_decode_attn is exactly
+ * prepare + partials + merge). Splitting them lets a caller time each step, or
+ * exchange the per-chunk partial states before merging (e.g. when the
+ * sequence is sharded over several devices).
+ *
+ * lrkv_decode_prepare: query preparation. RoPE mode: combines q (un-rotated,
+ *   float32 [batch][Hq][head_dim]) with bk into the workspace; other modes:
+ *   nothing to do (returns LRKV_OK after validation).
+ * lrkv_decode_partials: streams the cache chunk by chunk and writes each
+ *   chunk's softmax state (running max, running sum, unnormalised output) to
+ *   the workspace. RoPE mode reads the prepared queries (q may be NULL) and
+ *   q_pos; the absorbed and hybrid modes read q and sm_scale.
+ * lrkv_merge_partials: merges the chunk states by online softmax into out.
+ *
+ * Errors as for lrkv_decode_attn.
+ */
+int32_t lrkv_decode_prepare(int32_t mode, const void *cache, const float *q, const void *bk,
+                            float sm_scale, void *workspace, size_t ws_bytes, int32_t host_max_len,
+                            int32_t n_split, void *stream);
+int32_t lrkv_decode_partials(int32_t mode, const void *cache, const float *q, const int32_t *q_pos,
+                             float sm_scale, void *workspace, size_t ws_bytes, int32_t host_max_len,
+                             int32_t n_split, void *stream);
+int32_t lrkv_merge_partials(int32_t mode, const void *cache, float *out, void *workspace,
+                            size_t ws_bytes, int32_t host_max_len, int32_t n_split, void *stream);
+
+/*
  * Factor pages of a hybrid cache: for each (b, kv_head, page) triple in
  * `pages` (device int32 [n_pages][3]) and for K and V separately, form the
  * Gram matrix G = X X^T of the P x head_dim page X, take its top-r eigenvectors

@@ -27,7 +27,8 @@ BLOCK = 32
 
 EXPORTS = (
     "lrkv_status_string", "lrkv_version", "lrkv_decode_workspace_bytes", "lrkv_append_latent",
-    "lrkv_decode_attn", "lrkv_factor_page", "lrkv_paged_plan",
+    "lrkv_decode_attn", "lrkv_decode_prepare", "lrkv_decode_partials", "lrkv_merge_partials",
+    "lrkv_factor_page", "lrkv_paged_plan",
 )
 
 c_i32 = ctypes.c_int32
@@ -80,6 +81,14 @@ def lib() -> ctypes.CDLL:
         L.lrkv_decode_attn.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp,
                                        ctypes.c_size_t, c_i32, c_i32, c_vp]
         L.lrkv_decode_attn.restype = c_i32
+        L.lrkv_decode_prepare.argtypes = [c_i32, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, ctypes.c_size_t,
+                                          c_i32, c_i32, c_vp]
+        L.lrkv_decode_prepare.restype = c_i32
+        L.lrkv_decode_partials.argtypes = [c_i32, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, ctypes.c_size_t,
+                                           c_i32, c_i32, c_vp]
+        L.lrkv_decode_partials.restype = c_i32
+        L.lrkv_merge_partials.argtypes = [c_i32, c_vp, c_vp, c_vp, ctypes.c_size_t, c_i32, c_i32, c_vp]
+        L.lrkv_merge_partials.restype = c_i32
         L.lrkv_factor_page.argtypes = [ctypes.POINTER(PagedCacheDesc), c_vp, c_i32, c_vp, c_vp,
                                        c_i32, c_i32, c_vp]
         L.lrkv_factor_page.restype = c_i32

@@ -17,7 +17,8 @@ from ._lib import (BLOCK, FMT_FP16, FMT_INT4_G32, MODE_ABSORBED, MODE_HYBRID_PAG
                    MODE_ROPE_RECON, PAGE_EMPTY, LatentCacheDesc, PagedCacheDesc, LrkvError)
 
 __all__ = [
-    "decode_workspace_bytes", "append_latent", "decode_attn", "factor_page", "paged_plan",
+    "decode_workspace_bytes", "append_latent", "decode_attn", "decode_prepare", "decode_partials",
+    "merge_partials", "factor_page", "paged_plan",
     "LatentCache", "PagedCache", "LrkvError",
     "MODE_ROPE_RECON", "MODE_ABSORBED", "MODE_HYBRID_PAGED", "FMT_FP16", "FMT_INT4_G32",
 ]
@@ -55,6 +56,31 @@ def decode_attn(mode: int, desc, q, bk, q_pos, sm_scale: float, out, workspace,
     L.check(L.lib().lrkv_decode_attn(mode, ctypes.byref(desc), _p(q), _p(bk), _p(q_pos),
                                      float(sm_scale), _p(out), _p(workspace), ws_bytes,
                                      host_max_len, n_split, _stream(stream)), "lrkv_decode_attn")
+
+
+def _ws(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def decode_prepare(mode: int, desc, q, bk, sm_scale: float, workspace, host_max_len: int,
+                   n_split: int = 0, stream=None) -> None:
+    L.check(L.lib().lrkv_decode_prepare(mode, ctypes.byref(desc), _p(q), _p(bk), float(sm_scale),
+                                        _p(workspace), _ws(workspace), host_max_len, n_split,
+                                        _stream(stream)), "lrkv_decode_prepare")
+
+
+def decode_partials(mode: int, desc, q, q_pos, sm_scale: float, workspace, host_max_len: int,
+                    n_split: int = 0, stream=None) -> None:
+    L.check(L.lib().lrkv_decode_partials(mode, ctypes.byref(desc), _p(q), _p(q_pos), float(sm_scale),
+                                         _p(workspace), _ws(workspace), host_max_len, n_split,
+                                         _stream(stream)), "lrkv_decode_partials")
+
+
+def merge_partials(mode: int, desc, out, workspace, host_max_len: int, n_split: int = 0,
+                   stream=None) -> None:
+    L.check(L.lib().lrkv_merge_partials(mode, ctypes.byref(desc), _p(out), _p(workspace),
+                                        _ws(workspace), host_max_len, n_split, _stream(stream)),
+            "lrkv_merge_partials")
 
 
 def factor_page(desc, pages, n_pages: int, src_k=None, src_v=None, src_len: int = 0,

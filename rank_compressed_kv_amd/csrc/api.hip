@@ -27,33 +27,42 @@ LatentGeom latent_geom(const lrkv_latent_cache* c) {
 }
 
 // Chunking of the sequence: enough workgroups to cover the 256 compute units
-// a couple of times, chunks a multiple of the 32-token tile.
+// a couple of times, chunks a multiple of the 32-token tile. `cap_split` is an
+// upper bound of the split count for every length <= host_max_len, so that a
+// workspace sized for one length also serves every shorter one.
 static void pick_split(int per_split_groups, int host_max_len, int n_split, int target,
-                       int* out_split, int* out_chunk) {
+                       int max_chunk_tiles, int* out_split, int* out_chunk, int* cap_split) {
     const int tiles = (host_max_len + kTile - 1) / kTile;
-    if (n_split <= 0) {
-        n_split = (target + per_split_groups - 1) / per_split_groups;
-    }
+    if (n_split <= 0) n_split = (target + per_split_groups - 1) / per_split_groups;
+    const int min_split = (tiles + max_chunk_tiles - 1) / max_chunk_tiles;
+    if (n_split < min_split) n_split = min_split;
+    if (n_split > kMaxSplit) n_split = kMaxSplit;
     if (n_split > tiles) n_split = tiles;
     if (n_split < 1) n_split = 1;
     const int chunk_tiles = (tiles + n_split - 1) / n_split;
     *out_chunk = chunk_tiles * kTile;
     *out_split = (tiles + chunk_tiles - 1) / chunk_tiles;
+    *cap_split = n_split;
 }
 
 LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len, int n_split) {
     LatentWorkspace w;
-    const int target = mode == LRKV_MODE_ROPE_RECON ? 512 : 1024;
-    pick_split(g.B * g.U, host_max_len, n_split, target, &w.n_split, &w.chunk);
+    // RoPE: ~256 (chunk, unit, sequence) groups, each split over the unit's head
+    // groups; absorbed: ~1024 workgroups of 4 independent waves
+    const int target = mode == LRKV_MODE_ROPE_RECON ? 256 : 1024;
+    int cap_split = 1;
+    const int max_chunk_tiles = mode == LRKV_MODE_ROPE_RECON ? kMaxRopeTiles : 1 << 30;
+    pick_split(g.B * g.U, host_max_len, n_split, target, max_chunk_tiles, &w.n_split, &w.chunk,
+               &cap_split);
     size_t off = 0;
     w.part_off = off;
-    off += align_up((size_t)g.B * g.Hq * w.n_split * (g.r + 2) * sizeof(float), 256);
+    off += align_up((size_t)g.B * g.Hq * cap_split * (g.r + 2) * sizeof(float), 256);
     w.qp_off = off;
     w.qs_off = off;
     if (mode == LRKV_MODE_ROPE_RECON) {
         off += align_up((size_t)g.B * g.Hq * g.dh * g.r * sizeof(half_t), 256);
         w.qs_off = off;
-        off += align_up((size_t)g.B * g.Hq * sizeof(float), 256);
+        off += align_up((size_t)g.B * g.U * (g.dh / 2) * sizeof(float), 256);
     }
     w.total = off;
     return w;
@@ -64,14 +73,13 @@ PagedWorkspace paged_workspace(const lrkv_paged_cache* c, int host_max_len, int 
     const int npg = (host_max_len + c->page_size - 1) / c->page_size;
     const int groups = c->batch * c->kv_heads;
     if (n_split <= 0) n_split = (2048 + groups - 1) / groups;
+    if (n_split > kMaxSplit) n_split = kMaxSplit;
     if (n_split > npg) n_split = npg;
     if (n_split < 1) n_split = 1;
     w.pages_per_split = (npg + n_split - 1) / n_split;
-    if (w.pages_per_split < 1) w.pages_per_split = 1;
     w.n_split = (npg + w.pages_per_split - 1) / w.pages_per_split;
-    if (w.n_split < 1) w.n_split = 1;
     w.part_off = 0;
-    w.total = align_up((size_t)c->batch * c->kv_heads * c->q_per_kv * w.n_split *
+    w.total = align_up((size_t)c->batch * c->kv_heads * c->q_per_kv * n_split *
                            (c->head_dim + 2) * sizeof(float), 256);
     return w;
 }
@@ -169,21 +177,29 @@ int32_t lrkv_append_latent(int32_t mode, const void* cache, const void* new_k, c
     return launch_append_latent(c, (const float*)new_k, (const float*)new_v, n_new, st);
 }
 
-int32_t lrkv_decode_attn(int32_t mode, const void* cache, const float* q, const void* bk,
-                         const int32_t* q_pos, float sm_scale, float* out, void* workspace,
-                         size_t ws_bytes, int32_t host_max_len, int32_t n_split, void* stream) {
-    if (!cache || !q || !out || host_max_len < 1) return LRKV_ERR_INVALID_ARG;
+}  // extern "C"
+
+// Shared validation and dispatch of the decode entry points. `phases` selects
+// which of prepare / partials / merge are enqueued; the pointers each phase
+// needs are checked here.
+static int32_t decode_common(int32_t mode, int phases, const void* cache, const float* q,
+                             const void* bk, const int32_t* q_pos, float sm_scale, float* out,
+                             void* workspace, size_t ws_bytes, int32_t host_max_len, int32_t n_split,
+                             void* stream) {
+    if (!cache || host_max_len < 1) return LRKV_ERR_INVALID_ARG;
+    if ((phases & kPhaseMerge) && !out) return LRKV_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
     if (mode == LRKV_MODE_HYBRID_PAGED) {
         const lrkv_paged_cache* c = (const lrkv_paged_cache*)cache;
         int32_t rc = check_paged(c);
         if (rc != LRKV_OK) return rc;
         if (bk || q_pos) return LRKV_ERR_INVALID_ARG;
+        if ((phases & kPhasePartials) && !q) return LRKV_ERR_INVALID_ARG;
         if (host_max_len > c->max_pages * c->page_size) return LRKV_ERR_INVALID_ARG;
         const PagedWorkspace w = paged_workspace(c, host_max_len, n_split);
         if (!workspace || ws_bytes < w.total || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
         const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
-        return launch_decode_hybrid(c, q, scale, out, workspace, w, st);
+        return launch_decode_hybrid(phases, c, q, scale, out, workspace, w, st);
     }
     if (mode != LRKV_MODE_ROPE_RECON && mode != LRKV_MODE_ABSORBED) return LRKV_ERR_INVALID_ARG;
     const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
@@ -191,9 +207,10 @@ int32_t lrkv_decode_attn(int32_t mode, const void* cache, const float* q, const 
     if (rc != LRKV_OK) return rc;
     if (host_max_len > c->capacity) return LRKV_ERR_INVALID_ARG;
     if (mode == LRKV_MODE_ROPE_RECON) {
-        if (!bk) return LRKV_ERR_INVALID_ARG;
-    } else if (bk || q_pos) {
-        return LRKV_ERR_INVALID_ARG;
+        if ((phases & kPhasePrepare) && (!bk || !q)) return LRKV_ERR_INVALID_ARG;
+    } else {
+        if (bk || q_pos) return LRKV_ERR_INVALID_ARG;
+        if ((phases & kPhasePartials) && !q) return LRKV_ERR_INVALID_ARG;
     }
     const LatentGeom g = latent_geom(c);
     if (g.r % 32) return LRKV_ERR_UNSUPPORTED;
@@ -201,7 +218,38 @@ int32_t lrkv_decode_attn(int32_t mode, const void* cache, const float* q, const 
     const LatentWorkspace w = latent_workspace(mode, g, host_max_len, n_split);
     if (!workspace || ws_bytes < w.total || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
-    return launch_decode_latent(mode, c, q, (const half_t*)bk, q_pos, scale, out, workspace, w, st);
+    return launch_decode_latent(mode, phases, c, q, (const half_t*)bk, q_pos, scale, out, workspace,
+                                w, st);
+}
+
+extern "C" {
+
+int32_t lrkv_decode_attn(int32_t mode, const void* cache, const float* q, const void* bk,
+                         const int32_t* q_pos, float sm_scale, float* out, void* workspace,
+                         size_t ws_bytes, int32_t host_max_len, int32_t n_split, void* stream) {
+    if (!q) return LRKV_ERR_INVALID_ARG;
+    return decode_common(mode, kPhaseAll, cache, q, bk, q_pos, sm_scale, out, workspace, ws_bytes,
+                         host_max_len, n_split, stream);
+}
+
+int32_t lrkv_decode_prepare(int32_t mode, const void* cache, const float* q, const void* bk,
+                            float sm_scale, void* workspace, size_t ws_bytes, int32_t host_max_len,
+                            int32_t n_split, void* stream) {
+    return decode_common(mode, kPhasePrepare, cache, q, bk, nullptr, sm_scale, nullptr, workspace,
+                         ws_bytes, host_max_len, n_split, stream);
+}
+
+int32_t lrkv_decode_partials(int32_t mode, const void* cache, const float* q, const int32_t* q_pos,
+                             float sm_scale, void* workspace, size_t ws_bytes, int32_t host_max_len,
+                             int32_t n_split, void* stream) {
+    return decode_common(mode, kPhasePartials, cache, q, nullptr, q_pos, sm_scale, nullptr,
+                         workspace, ws_bytes, host_max_len, n_split, stream);
+}
+
+int32_t lrkv_merge_partials(int32_t mode, const void* cache, float* out, void* workspace,
+                            size_t ws_bytes, int32_t host_max_len, int32_t n_split, void* stream) {
+    return decode_common(mode, kPhaseMerge, cache, nullptr, nullptr, nullptr, 0.0f, out, workspace,
+                         ws_bytes, host_max_len, n_split, stream);
 }
 
 int32_t lrkv_factor_page(const lrkv_paged_cache* cache, const int32_t* pages, int32_t n_pages,

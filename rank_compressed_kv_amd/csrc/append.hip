@@ -48,6 +48,38 @@ __global__ void append_fp16(const float* __restrict__ nk, const float* __restric
     for (int k = 0; k < 8; ++k) vblk[k * kTile] = (half_t)vv[k];
 }
 
+// Decode-size fp16 append in one workgroup: every thread reads lens before the
+// workgroup barrier, so the same kernel can bump the lengths afterwards.
+__global__ __launch_bounds__(256) void append_fp16_small(const float* __restrict__ nk,
+                                                         const float* __restrict__ nv,
+                                                         half_t* __restrict__ hk,
+                                                         half_t* __restrict__ hv,
+                                                         int32_t* __restrict__ lens, int B, int U,
+                                                         int r, int cap, int n_new) {
+    const int r8 = r / 8;
+    const int total = B * U * n_new * r8;
+    for (int e = threadIdx.x; e < total; e += blockDim.x) {
+        const int d8 = e % r8;
+        int rest = e / r8;
+        const int i = rest % n_new;
+        rest /= n_new;
+        const int u = rest % U;
+        const int b = rest / U;
+        const int pos = lens[b] + i;
+        const long src = (((long)b * U + u) * n_new + i) * r + d8 * 8;
+        const long bu = (long)b * U + u;
+        half8 kh;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) kh[k] = (half_t)nk[src + k];
+        *reinterpret_cast<half8*>(hk + (bu * cap + pos) * r + d8 * 8) = kh;
+        half_t* vblk = hv + ((bu * (cap / kTile) + pos / kTile) * r + d8 * 8) * kTile + pos % kTile;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vblk[k * kTile] = (half_t)nv[src + k];
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] += n_new;
+}
+
 // The codec of one 32-element group: fp16 scale and the 32 codes.
 __device__ void quant_group(const float* __restrict__ x, int* codes, half_t* scale) {
     float amax = 0.0f;
@@ -182,6 +214,11 @@ inline unsigned blocks_for(long n, int bs) { return (unsigned)((n + bs - 1) / bs
 int32_t launch_append_latent(const lrkv_latent_cache* c, const float* nk, const float* nv,
                              int n_new, hipStream_t st) {
     const int B = c->batch, U = c->units, r = c->rank, cap = c->capacity;
+    if (c->fmt == LRKV_FMT_FP16 && (long)B * U * n_new * (r / 8) <= 1024) {
+        hipLaunchKernelGGL(append_fp16_small, dim3(1), dim3(256), 0, st, nk, nv, (half_t*)c->hk,
+                           (half_t*)c->hv, c->lens, B, U, r, cap, n_new);
+        return last_launch_status();
+    }
     if (c->fmt == LRKV_FMT_FP16) {
         const long n = (long)B * U * n_new * (r / 8);
         hipLaunchKernelGGL(append_fp16, dim3(blocks_for(n, 256)), dim3(256), 0, st, nk, nv,

@@ -17,6 +17,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kTile = 32;          // tokens per attention tile == cache block
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSplit = 1024;    // sequence chunks merged per head (merge kernel's LDS)
+constexpr int kMaxRopeTiles = 256; // tiles per RoPE chunk: bounds the angle-rotation drift
 
 // ---------------------------------------------------------------- MFMA wrappers
 // v_mfma_f32_32x32x16_f16. Lane l supplies A[l%32][8*(l/32) + 0..7] and
@@ -72,7 +74,7 @@ LatentGeom latent_geom(const lrkv_latent_cache* c);
 
 // Decode workspace for the Palu modes: partials [B][Hq][n_split][r + 2] float,
 // then (RoPE mode) the rotated-basis queries [B][Hq][dh][r] half and their
-// scales [B][Hq] float.
+// per-frequency scales [B][U][dh/2] float.
 struct LatentWorkspace {
     size_t part_off, qp_off, qs_off, total;
     int n_split, chunk;
@@ -83,7 +85,10 @@ int32_t launch_append_latent(const lrkv_latent_cache* c, const float* nk, const 
                              int n_new, hipStream_t st);
 int32_t launch_append_paged(const lrkv_paged_cache* c, const half_t* nk, const half_t* nv,
                             int n_new, hipStream_t st);
-int32_t launch_decode_latent(int mode, const lrkv_latent_cache* c, const float* q,
+// Decode phases: query preparation, per-chunk partial states, split merge.
+constexpr int kPhasePrepare = 1, kPhasePartials = 2, kPhaseMerge = 4, kPhaseAll = 7;
+
+int32_t launch_decode_latent(int mode, int phases, const lrkv_latent_cache* c, const float* q,
                              const half_t* bk, const int32_t* q_pos, float sm_scale, float* out,
                              void* ws, const LatentWorkspace& w, hipStream_t st);
 
@@ -92,8 +97,8 @@ struct PagedWorkspace {
     int n_split, pages_per_split;
 };
 PagedWorkspace paged_workspace(const lrkv_paged_cache* c, int host_max_len, int n_split);
-int32_t launch_decode_hybrid(const lrkv_paged_cache* c, const float* q, float sm_scale, float* out,
-                             void* ws, const PagedWorkspace& w, hipStream_t st);
+int32_t launch_decode_hybrid(int phases, const lrkv_paged_cache* c, const float* q, float sm_scale,
+                             float* out, void* ws, const PagedWorkspace& w, hipStream_t st);
 int32_t launch_factor_page(const lrkv_paged_cache* c, const int32_t* pages, int n_pages,
                            const half_t* src_k, const half_t* src_v, int src_len, int max_sweeps,
                            hipStream_t st);

@@ -192,16 +192,18 @@ __global__ __launch_bounds__(256, 2) void hybrid_decode(const HybridArgs a) {
 
 void launch_merge(const float* part, float* out, int BH, int n_split, int D, hipStream_t st);
 
-int32_t launch_decode_hybrid(const lrkv_paged_cache* c, const float* q, float sm_scale, float* out,
-                             void* ws, const PagedWorkspace& w, hipStream_t st) {
+int32_t launch_decode_hybrid(int phases, const lrkv_paged_cache* c, const float* q, float sm_scale,
+                             float* out, void* ws, const PagedWorkspace& w, hipStream_t st) {
     float* part = (float*)((char*)ws + w.part_off);
     HybridArgs a{(const half_t*)c->dense_k, (const half_t*)c->dense_v, (const half_t*)c->lk,
                  (const half_t*)c->rk, (const half_t*)c->lv, (const half_t*)c->rv, c->page_table,
                  c->lens, q, part, c->kv_heads, c->q_per_kv, c->page_size, c->sink_pages,
                  c->window_pages, c->rank_k, c->rank_v, c->max_pages, w.n_split,
                  w.pages_per_split, sm_scale * kLog2e};
-    hipLaunchKernelGGL(hybrid_decode<128>, dim3(w.n_split, c->kv_heads, c->batch), dim3(256), 0, st, a);
-    launch_merge(part, out, c->batch * c->kv_heads * c->q_per_kv, w.n_split, c->head_dim, st);
+    if (phases & kPhasePartials)
+        hipLaunchKernelGGL(hybrid_decode<128>, dim3(w.n_split, c->kv_heads, c->batch), dim3(256), 0, st, a);
+    if (phases & kPhaseMerge)
+        launch_merge(part, out, c->batch * c->kv_heads * c->q_per_kv, w.n_split, c->head_dim, st);
     return last_launch_status();
 }
 

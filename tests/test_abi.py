@@ -141,3 +141,23 @@ def test_paged_plan_matches_oracle_page_states(lib):
     d5 = _paged(batch=8, kv_heads=8, max_pages=1024)
     assert lib.lrkv_paged_plan(ctypes.byref(d5), np.zeros(8, np.int32).ctypes.data, 32768, None, 0) == 8 * 8 * 1019
     assert lib.lrkv_paged_plan(ctypes.byref(d5), np.zeros(8, np.int32).ctypes.data, 32769 + 1024 * 32, None, 0) < 0
+
+
+def test_workspace_monotone_in_length(lib):
+    """A workspace sized for a length serves every shorter length (any split count)."""
+    for mode in (0, 1):
+        d = _latent(capacity=70000 // 32 * 32)
+        prev = 0
+        for T in list(range(1, 3000, 37)) + list(range(65000, 69000, 33)):
+            for ns in (0, 1, 7, 64):
+                n = lib.lrkv_decode_workspace_bytes(mode, ctypes.byref(d), T, ns)
+                assert n > 0
+            n = lib.lrkv_decode_workspace_bytes(mode, ctypes.byref(d), T, 0)
+            assert n >= prev
+            prev = n
+    d = _paged(max_pages=2000)
+    prev = 0
+    for T in range(1, 64000, 311):
+        n = lib.lrkv_decode_workspace_bytes(2, ctypes.byref(d), T, 0)
+        assert n >= prev
+        prev = n
