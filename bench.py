@@ -156,10 +156,10 @@ def main() -> int:
         if timed:
             ev[1].record()
             lens_timed.append(L)
-        lrkv.decode_prepare(mode, c.desc, q, Bk, 0.0, w, L, args.n_split)
+        lrkv.decode_prepare(mode, c.desc, q, Bk, None, 0.0, w, L, args.n_split)
         if timed:
             ev[2].record()
-        lrkv.decode_partials(mode, c.desc, None, None, 0.0, w, L, args.n_split)
+        lrkv.decode_partials(mode, c.desc, None, 0.0, w, L, args.n_split)
         if timed:
             ev[3].record()
         lrkv.merge_partials(mode, c.desc, out, w, L, args.n_split)

@@ -206,21 +206,22 @@ int32_t lrkv_decode_attn(int32_t mode, const void *cache, const float *q, const 
  * sequence is sharded over several devices).
  *
  * lrkv_decode_prepare: query preparation. RoPE mode: combines q (un-rotated,
- *   float32 [batch][Hq][head_dim]) with bk into the workspace; other modes:
- *   nothing to do (returns LRKV_OK after validation).
+ *   float32 [batch][Hq][head_dim]) with bk, and builds the RoPE angle tables for
+ *   q_pos (NULL: lens[b] - 1), in the workspace; other modes: nothing to do
+ *   (returns LRKV_OK after validation).
  * lrkv_decode_partials: streams the cache chunk by chunk and writes each
  *   chunk's softmax state (running max, running sum, unnormalised output) to
- *   the workspace. RoPE mode reads the prepared queries (q may be NULL) and
- *   q_pos; the absorbed and hybrid modes read q and sm_scale.
+ *   the workspace. RoPE mode reads what prepare wrote (q may be NULL); the
+ *   absorbed and hybrid modes read q and sm_scale.
  * lrkv_merge_partials: merges the chunk states by online softmax into out.
  *
  * Errors as for lrkv_decode_attn.
  */
 int32_t lrkv_decode_prepare(int32_t mode, const void *cache, const float *q, const void *bk,
-                            float sm_scale, void *workspace, size_t ws_bytes, int32_t host_max_len,
-                            int32_t n_split, void *stream);
-int32_t lrkv_decode_partials(int32_t mode, const void *cache, const float *q, const int32_t *q_pos,
-                             float sm_scale, void *workspace, size_t ws_bytes, int32_t host_max_len,
+                            const int32_t *q_pos, float sm_scale, void *workspace, size_t ws_bytes,
+                            int32_t host_max_len, int32_t n_split, void *stream);
+int32_t lrkv_decode_partials(int32_t mode, const void *cache, const float *q, float sm_scale,
+                             void *workspace, size_t ws_bytes, int32_t host_max_len,
                              int32_t n_split, void *stream);
 int32_t lrkv_merge_partials(int32_t mode, const void *cache, float *out, void *workspace,
                             size_t ws_bytes, int32_t host_max_len, int32_t n_split, void *stream);

@@ -81,10 +81,10 @@ def lib() -> ctypes.CDLL:
         L.lrkv_decode_attn.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp,
                                        ctypes.c_size_t, c_i32, c_i32, c_vp]
         L.lrkv_decode_attn.restype = c_i32
-        L.lrkv_decode_prepare.argtypes = [c_i32, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, ctypes.c_size_t,
-                                          c_i32, c_i32, c_vp]
+        L.lrkv_decode_prepare.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp,
+                                          ctypes.c_size_t, c_i32, c_i32, c_vp]
         L.lrkv_decode_prepare.restype = c_i32
-        L.lrkv_decode_partials.argtypes = [c_i32, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, ctypes.c_size_t,
+        L.lrkv_decode_partials.argtypes = [c_i32, c_vp, c_vp, ctypes.c_float, c_vp, ctypes.c_size_t,
                                            c_i32, c_i32, c_vp]
         L.lrkv_decode_partials.restype = c_i32
         L.lrkv_merge_partials.argtypes = [c_i32, c_vp, c_vp, c_vp, ctypes.c_size_t, c_i32, c_i32, c_vp]

@@ -62,16 +62,16 @@ def _ws(workspace):
     return 0 if workspace is None else workspace.numel() * workspace.element_size()
 
 
-def decode_prepare(mode: int, desc, q, bk, sm_scale: float, workspace, host_max_len: int,
+def decode_prepare(mode: int, desc, q, bk, q_pos, sm_scale: float, workspace, host_max_len: int,
                    n_split: int = 0, stream=None) -> None:
-    L.check(L.lib().lrkv_decode_prepare(mode, ctypes.byref(desc), _p(q), _p(bk), float(sm_scale),
-                                        _p(workspace), _ws(workspace), host_max_len, n_split,
-                                        _stream(stream)), "lrkv_decode_prepare")
+    L.check(L.lib().lrkv_decode_prepare(mode, ctypes.byref(desc), _p(q), _p(bk), _p(q_pos),
+                                        float(sm_scale), _p(workspace), _ws(workspace), host_max_len,
+                                        n_split, _stream(stream)), "lrkv_decode_prepare")
 
 
-def decode_partials(mode: int, desc, q, q_pos, sm_scale: float, workspace, host_max_len: int,
+def decode_partials(mode: int, desc, q, sm_scale: float, workspace, host_max_len: int,
                     n_split: int = 0, stream=None) -> None:
-    L.check(L.lib().lrkv_decode_partials(mode, ctypes.byref(desc), _p(q), _p(q_pos), float(sm_scale),
+    L.check(L.lib().lrkv_decode_partials(mode, ctypes.byref(desc), _p(q), float(sm_scale),
                                          _p(workspace), _ws(workspace), host_max_len, n_split,
                                          _stream(stream)), "lrkv_decode_partials")
 

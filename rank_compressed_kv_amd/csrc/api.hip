@@ -59,10 +59,13 @@ LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len
     off += align_up((size_t)g.B * g.Hq * cap_split * (g.r + 2) * sizeof(float), 256);
     w.qp_off = off;
     w.qs_off = off;
+    w.ang_off = off;
     if (mode == LRKV_MODE_ROPE_RECON) {
         off += align_up((size_t)g.B * g.Hq * g.dh * g.r * sizeof(half_t), 256);
         w.qs_off = off;
         off += align_up((size_t)g.B * g.U * (g.dh / 2) * sizeof(float), 256);
+        w.ang_off = off;
+        off += align_up((size_t)(33 + g.B * cap_split) * (g.dh / 2) * 2 * sizeof(float), 256);
     }
     w.total = off;
     return w;
@@ -233,16 +236,16 @@ int32_t lrkv_decode_attn(int32_t mode, const void* cache, const float* q, const 
 }
 
 int32_t lrkv_decode_prepare(int32_t mode, const void* cache, const float* q, const void* bk,
-                            float sm_scale, void* workspace, size_t ws_bytes, int32_t host_max_len,
-                            int32_t n_split, void* stream) {
-    return decode_common(mode, kPhasePrepare, cache, q, bk, nullptr, sm_scale, nullptr, workspace,
+                            const int32_t* q_pos, float sm_scale, void* workspace, size_t ws_bytes,
+                            int32_t host_max_len, int32_t n_split, void* stream) {
+    return decode_common(mode, kPhasePrepare, cache, q, bk, q_pos, sm_scale, nullptr, workspace,
                          ws_bytes, host_max_len, n_split, stream);
 }
 
-int32_t lrkv_decode_partials(int32_t mode, const void* cache, const float* q, const int32_t* q_pos,
-                             float sm_scale, void* workspace, size_t ws_bytes, int32_t host_max_len,
+int32_t lrkv_decode_partials(int32_t mode, const void* cache, const float* q, float sm_scale,
+                             void* workspace, size_t ws_bytes, int32_t host_max_len,
                              int32_t n_split, void* stream) {
-    return decode_common(mode, kPhasePartials, cache, q, nullptr, q_pos, sm_scale, nullptr,
+    return decode_common(mode, kPhasePartials, cache, q, nullptr, nullptr, sm_scale, nullptr,
                          workspace, ws_bytes, host_max_len, n_split, stream);
 }
 

@@ -73,10 +73,11 @@ struct LatentGeom {
 LatentGeom latent_geom(const lrkv_latent_cache* c);
 
 // Decode workspace for the Palu modes: partials [B][Hq][n_split][r + 2] float,
-// then (RoPE mode) the rotated-basis queries [B][Hq][dh][r] half and their
-// per-frequency scales [B][U][dh/2] float.
+// then (RoPE mode) the rotated-basis queries [B][Hq][dh][r] half, their
+// per-frequency scales [B][U][dh/2] float and the angle tables
+// [33 + B * n_split][dh/2] float2.
 struct LatentWorkspace {
-    size_t part_off, qp_off, qs_off, total;
+    size_t part_off, qp_off, qs_off, ang_off, total;
     int n_split, chunk;
 };
 LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len, int n_split);

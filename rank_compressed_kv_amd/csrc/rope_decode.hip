@@ -1,0 +1,507 @@
+// Reconstruct-with-RoPE decode attention over a Palu latent cache (gfx950).
+//
+// Palu digest, Method details: keys are cached as latents H^k and rebuilt on
+// chip as K = H^k B^k, RoPE is applied at each token's position, the query
+// attends, and the output stays in latent space, o = p H^v (B^v is folded into
+// W^o offline). Palu digest, Appendix: the sequence is tiled along its length
+// and each tile is reconstructed and scored on chip.
+//
+// Per 32-token tile and query head, the reconstruction GEMM H_tile B (r -> d_h)
+// runs in the query-rotated basis Q' prepared by rope_prep (same MFMA work per
+// token); RoPE is then one FMA per feature with the tile's cos/sin, which are
+// shared by all heads of the unit. Scores feed an online softmax (log2 domain)
+// and p (fp16) x H^v runs on a 16x16x32 MFMA from the dim-major value block.
+// Each workgroup covers one sequence chunk of one unit and writes the chunk's
+// (running max, running sum, unnormalised output) per head; merge.hip combines
+// the chunks.
+#include "tiles.h"
+
+#include <math.h>
+
+namespace lrkv {
+
+struct RopeArgs {
+    const void* hk;
+    const void* hv;
+    const half_t* sk;
+    const half_t* sv;
+    const int32_t* lens;
+    const half_t* qp;     // [B][Hq][DH][R] rotated-basis queries, scaled
+    const float* qs;      // [B][U][DH/2] 2^-e scale of each frequency
+    AngleTables ang;
+    float* part;          // [B][Hq][n_split][R + 2]
+    int B, U, NH, cap, n_split, chunk, n_groups;
+};
+
+namespace {
+
+// The lane's 8 frequencies in M-tile mt: feature f = 32 mt + 8 i + 4 (l/32) + e is
+// the cos (e even) or sin (e odd) coefficient of frequency f / 2.
+__device__ __forceinline__ int lane_freq(int k, int mt, int lane) {
+    return 16 * mt + 4 * (k >> 1) + 2 * (lane >> 5) + (k & 1);
+}
+
+// Initial cos/sin (times the frequency's 2^-e) of the lane's token in the
+// chunk's first tile, and the per-tile rotation.
+__device__ __forceinline__ void init_angles(const RopeArgs& p, int b, int split, long bu, int mt,
+                                            int lane, int DH, float* cs, float* sn, float* stc,
+                                            float* sts) {
+    const int half = DH / 2;
+    const float2* start = p.ang.start + ((long)b * p.n_split + split) * half;
+    const float2* tok = p.ang.tok + (lane & 31) * half;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int f = lane_freq(k, mt, lane);
+        const float2 a = cmul(start[f], tok[f]);
+        const float sc = p.qs[bu * half + f];
+        cs[k] = a.x * sc;
+        sn[k] = a.y * sc;
+        const float2 st = p.ang.step[f];
+        stc[k] = st.x;
+        sts[k] = st.y;
+    }
+}
+
+__device__ __forceinline__ void rotate_angles(float* cs, float* sn, const float* stc, const float* sts) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float c2 = fmaf(cs[k], stc[k], -sn[k] * sts[k]);
+        const float s2 = fmaf(sn[k], stc[k], cs[k] * sts[k]);
+        cs[k] = c2;
+        sn[k] = s2;
+    }
+}
+
+// Partial score of one head from a 32x32 score accumulator: sum over this lane's
+// 16 features of cos/sin x accumulator, then over the two half-waves.
+__device__ __forceinline__ float rope_combine(const floatx16& acc, const float* cs, const float* sn) {
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+            ps = fmaf(cs[2 * i + e2], acc[4 * i + 2 * e2], ps);
+            ps = fmaf(sn[2 * i + e2], acc[4 * i + 2 * e2 + 1], ps);
+        }
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, ps), __builtin_bit_cast(int, ps),
+                                                    false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+__device__ void write_empty(float* part, long hstride, int nh, int R, int tid, int nthreads) {
+    for (int e = tid; e < nh * (R + 2); e += nthreads) {
+        const int h = e / (R + 2), c = e % (R + 2);
+        part[h * hstride + c] = c == 0 ? -INFINITY : 0.0f;
+    }
+}
+
+// ============================================================================ generic kernel
+// One workgroup (4 waves): NHW query heads of one unit over one chunk. Wave w
+// owns feature rows [32w, 32w+32) of each head's Q' (MFMA A fragments in
+// registers); the key tile is staged in LDS; partial scores are summed across
+// waves in LDS; every wave runs the same softmax; wave w owns latent dims
+// [r/4 w, r/4 (w+1)) of the value product. The NH/NHW workgroups of a (chunk,
+// unit) are dispatched 8 apart in block order, so they share an XCD's L2.
+template <int R, int DH, int NHW, bool INT4>
+__global__ __launch_bounds__(256, 2) void rope_decode(const RopeArgs p) {
+    constexpr int KS = R / 16;                 // K steps of the score MFMA
+    constexpr int MT = DH / 32;                // feature M-tiles per head (waves that score)
+    constexpr int VM = R / 16;                 // 16-dim M-tiles of the value MFMA
+    constexpr int VMW = (VM + 3) / 4;          // value M-tiles per wave
+    constexpr int LDK = R + 8;
+    static_assert(MT >= 1 && MT <= 4, "head_dim must be 32..128");
+    __shared__ __attribute__((aligned(16))) half_t ktile[2][32][LDK];
+    __shared__ float spart[4][32][NHW];
+    __shared__ half_t pbuf[4][NHW][32];
+
+    const int HG = p.NH / NHW;
+    const int id = blockIdx.x, xcd = id & 7, kq = id >> 3;
+    const int hg = kq % HG, g = (kq / HG) * 8 + xcd;
+    if (g >= p.n_groups) return;
+    const int split = g % p.n_split, u = (g / p.n_split) % p.U, b = g / (p.n_split * p.U);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int Hq = p.U * p.NH, j0 = u * p.NH + hg * NHW;
+    const int len = min(p.lens[b], p.cap);
+    const int t_begin = split * p.chunk;
+    const int t_end = min(len, t_begin + p.chunk);
+    const long bu = (long)b * p.U + u;
+    float* part = p.part + ((long)(b * Hq + j0) * p.n_split + split) * (R + 2);
+    const long hstride = (long)p.n_split * (R + 2);
+    if (t_begin >= t_end) {
+        write_empty(part, hstride, NHW, R, tid, 256);
+        return;
+    }
+
+    float cs[8], sn[8], stc[8], sts[8];
+    if (w < MT) init_angles(p, b, split, bu, w, l, DH, cs, sn, stc, sts);
+
+    half8 afrag[NHW][KS];
+    if (w < MT) {
+#pragma unroll
+        for (int h = 0; h < NHW; ++h) {
+            const half_t* src = p.qp + (((long)b * Hq + j0 + h) * DH + 32 * w + (l & 31)) * R + 8 * (l >> 5);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) afrag[h][kk] = *reinterpret_cast<const half8*>(src + 16 * kk);
+        }
+    }
+
+    float m_run[NHW], l_run[NHW];
+    floatx4 accv[VMW];
+#pragma unroll
+    for (int h = 0; h < NHW; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.0f; }
+#pragma unroll
+    for (int v = 0; v < VMW; ++v) accv[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int n_tiles = (t_end - t_begin + 31) / 32;
+    KStage<R, INT4> stage;
+#pragma unroll
+    for (int part_ = 0; part_ < 2; ++part_) {
+        stage.load(p.hk, p.sk, bu * p.cap, t_begin, t_end, tid, part_);
+        stage.template store<LDK>(ktile[0], tid, part_);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_tiles; ++it) {
+        const int t0 = t_begin + 32 * it;
+        const int buf = it & 1;
+        const bool more = it + 1 < n_tiles;
+        if (more) stage.load(p.hk, p.sk, bu * p.cap, t0 + 32, t_end, tid, 0);
+        if (w < MT) {
+            floatx16 acc[NHW];
+#pragma unroll
+            for (int h = 0; h < NHW; ++h) acc[h] = floatx16{};
+            const half_t* brow = &ktile[buf][l & 31][8 * (l >> 5)];
+            half8 bf = *reinterpret_cast<const half8*>(brow);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const half8 cur = bf;
+                if (kk + 1 < KS) bf = *reinterpret_cast<const half8*>(brow + 16 * (kk + 1));
+#pragma unroll
+                for (int h = 0; h < NHW; ++h) acc[h] = mfma32(afrag[h][kk], cur, acc[h]);
+            }
+#pragma unroll
+            for (int h = 0; h < NHW; ++h) {
+                const float ps = rope_combine(acc[h], cs, sn);
+                if (l < 32) spart[w][l][h] = ps;
+            }
+            rotate_angles(cs, sn, stc, sts);
+        }
+        half8 vfr[VMW];
+        const long blk_base = bu * (p.cap / kTile) + t0 / kTile;
+#pragma unroll
+        for (int v = 0; v < VMW; ++v) {
+            const int mv = w * VMW + v;
+            if (mv < VM) vfr[v] = load_vfrag<R, INT4>(p.hv, p.sv, blk_base, mv, l, t0, t_end);
+        }
+        if (more) {
+            stage.template store<LDK>(ktile[buf ^ 1], tid, 0);
+            stage.load(p.hk, p.sk, bu * p.cap, t0 + 32, t_end, tid, 1);
+        }
+        __syncthreads();
+
+        // online softmax (every wave, every head of the group; log2 domain)
+        const int tok = l & 31;
+        const bool valid = t0 + tok < t_end;
+        float alpha[NHW];
+#pragma unroll
+        for (int h = 0; h < NHW; ++h) {
+            float sc = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < MT; ++ww) sc += spart[ww][tok][h];
+            sc = valid ? sc : -INFINITY;
+            const float mn = fmaxf(m_run[h], half_max32(sc));
+            alpha[h] = exp2f(m_run[h] - mn);
+            const float pv = valid ? exp2f(sc - mn) : 0.0f;
+            l_run[h] = fmaf(l_run[h], alpha[h], half_sum32(pv));
+            m_run[h] = mn;
+            if (l < 32) pbuf[w][h][tok] = (half_t)pv;
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        // values: acc[dim][head] += V^T p
+        const int hn = l & 15;
+        float a_hn = 1.0f;
+#pragma unroll
+        for (int h = 0; h < NHW; ++h) if (hn == h) a_hn = alpha[h];
+        half8 pf = hn < NHW ? *reinterpret_cast<const half8*>(&pbuf[w][hn < NHW ? hn : 0][8 * (l >> 4)]) : half8{};
+#pragma unroll
+        for (int v = 0; v < VMW; ++v) {
+            const int mv = w * VMW + v;
+            if (mv < VM) {
+                accv[v] *= a_hn;
+                accv[v] = mfma16(vfr[v], pf, accv[v]);
+            }
+        }
+        if (more) stage.template store<LDK>(ktile[buf ^ 1], tid, 1);
+        __syncthreads();
+    }
+
+    if (tid < NHW) {
+        part[tid * hstride + 0] = m_run[tid];
+        part[tid * hstride + 1] = l_run[tid];
+    }
+    const int hn = l & 15;
+    if (hn < NHW) {
+#pragma unroll
+        for (int v = 0; v < VMW; ++v) {
+            const int mv = w * VMW + v;
+            if (mv < VM) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    part[hn * hstride + 2 + 16 * mv + 4 * (l >> 4) + e] = accv[v][e];
+            }
+        }
+    }
+}
+
+// ============================================================================ ping-pong kernel
+// fp16 latents, rank 256, head_dim 128, 4 query heads per unit. One workgroup
+// of 8 waves per (chunk, unit): group A (waves 0-3) serves heads 0-1, group B
+// (waves 4-7) heads 2-3, wave w owning feature rows [32 (w%4), +32) of its
+// group's Q' (128 VGPRs of A fragments). The groups run half a tile apart
+// between workgroup barriers:
+//     half-step 2i  : A scores tile i      | B softmax + values of tile i-1
+//     half-step 2i+1: B scores tile i      | A softmax + values of tile i
+// so each SIMD holds one wave issuing score MFMAs and one doing the softmax and
+// the value product. Key and value tiles are loaded once per workgroup with
+// direct global->LDS loads into four buffers, three tiles ahead (every wave
+// issues exactly 6 loads per tile, so the waits count loads):
+//   keys   32 rows of 512 B padded to 528 B (conflict-free B-fragment reads),
+//          written one row per half-wave; rows past t_end re-read the last
+//          valid row and are masked in the softmax;
+//   values the dim-major 32-token block, each 1 KB load covering one 16-dim
+//          M-tile with lane i of the load taking (dim i % 16, tokens 8 (i/16)+0..7),
+//          so the value A fragment of lane l is the 16 bytes at +16 l; tokens
+//          past t_end are zeroed in registers.
+// B fragments are read three K steps ahead of their MFMAs.
+template <int R>
+__global__ __launch_bounds__(512, 1) void rope_decode_pp(const RopeArgs p) {
+    constexpr int DH = 128, NG = 2, KS = R / 16, LDK = R + 8, NBUF = 4, AHEAD = 3;
+    constexpr int VMW = (R / 16) / 4;          // value M-tiles per wave
+    constexpr int LOADS = 6;                   // global->LDS loads per wave per tile
+    static_assert(R == 256, "ping-pong kernel covers rank 256");
+    __shared__ __attribute__((aligned(16))) half_t ktile[NBUF][32 * LDK];
+    __shared__ __attribute__((aligned(16))) half_t vtile[NBUF][R * 32];
+    __shared__ float spart[2][4][32][NG];
+    __shared__ __attribute__((aligned(16))) half_t pbuf[8][NG][32];
+    __shared__ float2 stab[4][2][8];           // per-tile rotation of (M-tile, half-wave)
+
+    const int g = blockIdx.x;
+    if (g >= p.n_groups) return;
+    const int split = g % p.n_split, u = (g / p.n_split) % p.U, b = g / (p.n_split * p.U);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int grp = w >> 2, mt = w & 3;
+    const int Hq = p.U * 4, j0 = u * 4 + grp * NG;
+    const int len = min(p.lens[b], p.cap);
+    const int t_begin = split * p.chunk;
+    const int t_end = min(len, t_begin + p.chunk);
+    const long bu = (long)b * p.U + u;
+    const long hstride = (long)p.n_split * (R + 2);
+    float* part = p.part + ((long)(b * Hq + j0) * p.n_split + split) * (R + 2);
+    if (t_begin >= t_end) {
+        write_empty(p.part + ((long)(b * Hq + u * 4) * p.n_split + split) * (R + 2), hstride, 4, R, tid, 512);
+        return;
+    }
+    const int n_tiles = (t_end - t_begin + 31) / 32;
+    const half_t* hk = (const half_t*)p.hk + bu * p.cap * R;
+    const half_t* hv = (const half_t*)p.hv + bu * p.cap * R;      // [cap/32][R][32]
+
+    auto issue_tile = [&](int tile) {
+        const int t0 = t_begin + 32 * tile, bsel = tile % NBUF;
+        // keys: rows 4w .. 4w+3, one row per half-wave (LDS address from uniform values)
+#pragma unroll 1
+        for (int n = 0; n < 4; ++n) {
+            const int hsel = n & 1, row = 4 * w + n;
+            if ((l >> 5) == hsel)
+                dma16_async(hk + (long)min(t0 + row, t_end - 1) * R + (l & 31) * 8,
+                            ktile[bsel] + row * LDK - hsel * 256);
+        }
+        // values: 1 KB M-tiles 2w, 2w+1 of the block
+        const half_t* vb = hv + (long)(t0 / kTile) * R * kTile;
+#pragma unroll 1
+        for (int n = 2 * w; n < 2 * w + 2; ++n)
+            dma16_async(vb + (16 * n + (l & 15)) * kTile + 8 * (l >> 4), vtile[bsel] + n * 512);
+    };
+
+    float cs[8], sn[8];
+    {
+        float stc[8], sts[8];
+        init_angles(p, b, split, bu, mt, l, DH, cs, sn, stc, sts);
+        if ((l & 31) == 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) stab[mt][l >> 5][k] = make_float2(stc[k], sts[k]);
+        }
+    }
+    half8 afrag[NG][KS];
+#pragma unroll
+    for (int h = 0; h < NG; ++h) {
+        const half_t* src = p.qp + (((long)b * Hq + j0 + h) * DH + 32 * mt + (l & 31)) * R + 8 * (l >> 5);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) afrag[h][kk] = *reinterpret_cast<const half8*>(src + 16 * kk);
+    }
+    float m_run[NG], l_run[NG];
+    floatx4 accv[VMW];
+#pragma unroll
+    for (int h = 0; h < NG; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.0f; }
+#pragma unroll
+    for (int v = 0; v < VMW; ++v) accv[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // query fragments and angle tables: a real s_waitcnt vmcnt(0), which the
+    // compiler's wait tracking sees, so it adds no waits for them inside the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    for (int t = 0; t < AHEAD && t < n_tiles; ++t) issue_tile(t);
+    // tile 0 complete: the loads of min(n_tiles, AHEAD) - 1 later tiles may remain
+    if (n_tiles >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (n_tiles == 2) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else wait_vmem();
+    __syncthreads();
+
+    for (int hs = 0; hs <= 2 * n_tiles; ++hs) {
+        if (hs & 1) {
+            // tile i+1 must have landed (i = (hs-1)/2); then fetch tile i+3
+            const int i = (hs - 1) / 2;
+            if (i + 2 < n_tiles) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+            else wait_vmem();
+            if (i + 3 < n_tiles) issue_tile(i + 3);
+        }
+        const bool score = grp == 0 ? ((hs & 1) == 0 && hs < 2 * n_tiles) : (hs & 1);
+        const bool soft = grp == 0 ? (hs & 1) : ((hs & 1) == 0 && hs >= 2);
+        if (score) {
+            const int tile = grp == 0 ? hs / 2 : (hs - 1) / 2;
+            const half_t* brow = ktile[tile % NBUF] + (l & 31) * LDK + 8 * (l >> 5);
+            floatx16 acc[NG];
+#pragma unroll
+            for (int h = 0; h < NG; ++h) acc[h] = floatx16{};
+            half8 bq[AHEAD];
+#pragma unroll
+            for (int a = 0; a < AHEAD; ++a) bq[a] = *reinterpret_cast<const half8*>(brow + 16 * a);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const half8 cur = bq[kk % AHEAD];
+                if (kk + AHEAD < KS) bq[kk % AHEAD] = *reinterpret_cast<const half8*>(brow + 16 * (kk + AHEAD));
+#pragma unroll
+                for (int h = 0; h < NG; ++h) acc[h] = mfma32(afrag[h][kk], cur, acc[h]);
+            }
+            // keep AHEAD fragment reads in flight: reads, then (2 MFMA, 1 read) ..., then MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int kk = 0; kk < KS - AHEAD; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NG * AHEAD, 0);
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                const float ps = rope_combine(acc[h], cs, sn);
+                if (l < 32) spart[grp][mt][l][h] = ps;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float2 st = stab[mt][l >> 5][k];
+                const float c2 = fmaf(cs[k], st.x, -sn[k] * st.y);
+                const float s2 = fmaf(sn[k], st.x, cs[k] * st.y);
+                cs[k] = c2;
+                sn[k] = s2;
+            }
+        } else if (soft) {
+            const int tile = grp == 0 ? (hs - 1) / 2 : hs / 2 - 1;
+            const int t0 = t_begin + 32 * tile;
+            const int tok = l & 31;
+            const bool valid = t0 + tok < t_end;
+            float alpha[NG];
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                float sc = spart[grp][0][tok][h] + spart[grp][1][tok][h] + spart[grp][2][tok][h] +
+                           spart[grp][3][tok][h];
+                sc = valid ? sc : -INFINITY;
+                const float mn = fmaxf(m_run[h], half_max32(sc));
+                alpha[h] = exp2f(m_run[h] - mn);
+                const float pv = valid ? exp2f(sc - mn) : 0.0f;
+                l_run[h] = fmaf(l_run[h], alpha[h], half_sum32(pv));
+                m_run[h] = mn;
+                if (l < 32) pbuf[w][h][tok] = (half_t)pv;
+            }
+            __builtin_amdgcn_wave_barrier();
+            const int hn = l & 15;
+            const float a_hn = hn == 0 ? alpha[0] : (hn == 1 ? alpha[1] : 1.0f);
+            const half8 pf = hn < NG ? *reinterpret_cast<const half8*>(&pbuf[w][hn < NG ? hn : 0][8 * (l >> 4)])
+                                     : half8{};
+            const half_t* vt = vtile[tile % NBUF];
+            const bool tail = t0 + 32 > t_end;
+#pragma unroll
+            for (int v = 0; v < VMW; ++v) {
+                const int mv = mt * VMW + v;
+                half8 a = *reinterpret_cast<const half8*>(vt + mv * 512 + 8 * l);
+                if (tail) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (t0 + 8 * (l >> 4) + e >= t_end) a[e] = (half_t)0.0f;
+                }
+                accv[v] *= a_hn;
+                accv[v] = mfma16(a, pf, accv[v]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (mt == 0 && l < NG) {
+        part[l * hstride + 0] = m_run[l];
+        part[l * hstride + 1] = l_run[l];
+    }
+    const int hn = l & 15;
+    if (hn < NG) {
+#pragma unroll
+        for (int v = 0; v < VMW; ++v) {
+            const int mv = mt * VMW + v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[hn * hstride + 2 + 16 * mv + 4 * (l >> 4) + e] = accv[v][e];
+        }
+    }
+}
+
+template <int R, int DH, int NHW, bool INT4>
+void launch_generic(RopeArgs a, hipStream_t st) {
+    a.n_groups = a.n_split * a.U * a.B;
+    const int slots = (a.n_groups + 7) / 8;
+    hipLaunchKernelGGL((rope_decode<R, DH, NHW, INT4>), dim3(slots * 8 * (a.NH / NHW)), dim3(256), 0, st, a);
+}
+
+}  // namespace
+
+bool rope_shape_supported(int r, int dh, int nh) {
+    return (r == 32 && dh == 64 && nh == 2) || (r == 64 && dh == 64 && nh == 2) ||
+           (r == 256 && dh == 128 && nh == 4) || (r == 64 && dh == 128 && nh == 4) ||
+           (r == 128 && dh == 128 && nh == 4);
+}
+
+int32_t launch_rope_decode(const lrkv_latent_cache* c, const half_t* qp, const float* qs,
+                           const float2* angles, float* part, int n_split, int chunk, hipStream_t st) {
+    const int nh = c->kv_per_unit * c->q_per_kv, r = c->rank, dh = c->head_dim;
+    const bool int4 = c->fmt == LRKV_FMT_INT4_G32;
+    RopeArgs a{c->hk, c->hv, (const half_t*)c->sk, (const half_t*)c->sv, c->lens, qp, qs,
+               AngleTables{angles, angles + dh / 2, angles + 33 * (dh / 2)}, part, c->batch,
+               c->units, nh, c->capacity, n_split, chunk, 0};
+    if (r == 256 && dh == 128 && nh == 4 && !int4) {
+        a.n_groups = n_split * a.U * a.B;
+        hipLaunchKernelGGL(rope_decode_pp<256>, dim3(a.n_groups), dim3(512), 0, st, a);
+        return LRKV_OK;
+    }
+    // heads per workgroup of the generic kernel: two for the larger ranks
+    // (register budget of two resident workgroups per CU)
+#define LRKV_ROPE(R_, DH_, NH_, NHW16_, NHW4_)                                               \
+    if (r == R_ && dh == DH_ && nh == NH_) {                                                \
+        if (int4) launch_generic<R_, DH_, NHW4_, true>(a, st);                               \
+        else launch_generic<R_, DH_, NHW16_, false>(a, st);                                  \
+        return LRKV_OK;                                                                      \
+    }
+    LRKV_ROPE(32, 64, 2, 2, 2)
+    LRKV_ROPE(64, 64, 2, 2, 2)
+    LRKV_ROPE(256, 128, 4, 1, 1)
+    LRKV_ROPE(64, 128, 4, 4, 4)
+    LRKV_ROPE(128, 128, 4, 2, 2)
+#undef LRKV_ROPE
+    return LRKV_ERR_UNSUPPORTED;
+}
+
+}  // namespace lrkv

@@ -1,0 +1,150 @@
+// Device helpers shared by the latent-cache decode kernels: lane reductions,
+// key-tile staging (registers or direct global->LDS), value fragments.
+#pragma once
+
+#include "common.h"
+
+namespace lrkv {
+
+// ---------------------------------------------------------------- reductions
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// v_permlane16_swap(v, v) returns {row 2k, row 2k+1} values in every lane of the
+// row pair, so their sum / max is the row-pair result.
+__device__ __forceinline__ float rowpair(float v, bool is_max) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                    false, false);
+    const float a = __builtin_bit_cast(float, (int)r[0]), b = __builtin_bit_cast(float, (int)r[1]);
+    return is_max ? fmaxf(a, b) : a + b;
+}
+// Sum / max over the 32 lanes of each half-wave: DPP within rows of 16
+// (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror), then the row pair.
+__device__ __forceinline__ float half_sum32(float v) {
+    v += dppf<0xB1>(v);
+    v += dppf<0x4E>(v);
+    v += dppf<0x141>(v);
+    v += dppf<0x140>(v);
+    return rowpair(v, false);
+}
+__device__ __forceinline__ float half_max32(float v) {
+    v = fmaxf(v, dppf<0xB1>(v));
+    v = fmaxf(v, dppf<0x4E>(v));
+    v = fmaxf(v, dppf<0x141>(v));
+    v = fmaxf(v, dppf<0x140>(v));
+    return rowpair(v, true);
+}
+
+// ---------------------------------------------------------------- direct global->LDS loads
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// One 16-byte load per active lane; lane i of the wave writes dst + 16 i. `dst`
+// must be built from wave-uniform values only.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The same load issued as inline assembly, so that the compiler does not treat
+// it as a store to LDS: it then inserts no vmcnt waits before later LDS reads,
+// and the caller orders the data itself (counted s_waitcnt vmcnt + barrier).
+// `dst` must be wave-uniform; M0 carries its LDS byte address.
+__device__ __forceinline__ void dma16_async(const void* src, const void* dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// ---------------------------------------------------------------- key tile, register staging
+// 32 tokens x R fp16 rows in LDS with rows padded to R + 8 halves; int4 codes are
+// dequantised on the way (code * scale rounded to fp16). Rows at or past t_end
+// are zero. Staged in two halves to halve the staging registers.
+template <int R, bool INT4>
+struct KStage {
+    static constexpr int NV = 32 * R / 8;                 // 8-dim items per tile
+    static constexpr int PER = (NV + 255) / 256;
+    static constexpr int HALF = (PER + 1) / 2;            // items staged per half
+    uint4 v[HALF];
+
+    __device__ __forceinline__ void load(const void* hk, const half_t* sk, long row0, int t0,
+                                         int t_end, int tid, int part) {
+#pragma unroll
+        for (int kk = 0; kk < HALF; ++kk) {
+            const int k = HALF * part + kk;
+            const int item = tid + 256 * k;
+            const int row = item / (R / 8), c8 = item % (R / 8);
+            v[kk] = make_uint4(0, 0, 0, 0);
+            if (k < PER && item < NV && t0 + row < t_end) {
+                const long tok = row0 + t0 + row;
+                if constexpr (!INT4) {
+                    v[kk] = *reinterpret_cast<const uint4*>((const half_t*)hk + tok * R + c8 * 8);
+                } else {
+                    const uint32_t code = *reinterpret_cast<const uint32_t*>((const uint8_t*)hk + tok * (R / 2) + c8 * 4);
+                    const float sc = (float)sk[tok * (R / 32) + c8 / 4];
+                    half8 h;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) h[e] = (half_t)((float)nibble(code, e) * sc);
+                    v[kk] = *reinterpret_cast<uint4*>(&h);
+                }
+            }
+        }
+    }
+    template <int LDK>
+    __device__ __forceinline__ void store(half_t (*tile)[LDK], int tid, int part) const {
+#pragma unroll
+        for (int kk = 0; kk < HALF; ++kk) {
+            const int k = HALF * part + kk;
+            const int item = tid + 256 * k;
+            if (k < PER && item < NV) {
+                const int row = item / (R / 8), c8 = item % (R / 8);
+                *reinterpret_cast<uint4*>(&tile[row][c8 * 8]) = v[kk];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------- value fragments
+// A fragment of V^T for the 16x16x32 MFMA from the dim-major 32-token block in
+// global memory: dims [16 mv, 16 mv + 16) x the 8 tokens of lane group l/16,
+// masked past t_end.
+template <int R, bool INT4>
+__device__ __forceinline__ half8 load_vfrag(const void* hv, const half_t* sv, long blk_base,
+                                            int mv, int lane, int tok0, int t_end) {
+    const int dim = 16 * mv + (lane & 15);
+    const int g = lane >> 4;
+    half8 a;
+    if constexpr (!INT4) {
+        a = *reinterpret_cast<const half8*>((const half_t*)hv + (blk_base * R + dim) * kTile + 8 * g);
+    } else {
+        const uint32_t code = *reinterpret_cast<const uint32_t*>((const uint8_t*)hv + (blk_base * R + dim) * (kTile / 2) + 4 * g);
+        const half8 sc = *reinterpret_cast<const half8*>(sv + (blk_base * (R / 32) + dim / 32) * kTile + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (half_t)((float)nibble(code, e) * (float)sc[e]);
+    }
+    const int first = tok0 + 8 * g;
+    if (first + 8 > t_end) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (first + e >= t_end) a[e] = (half_t)0.0f;
+    }
+    return a;
+}
+
+// ---------------------------------------------------------------- RoPE angles
+// Tables written by the query-preparation step (fp64 angles, fp32 values):
+//   step[f]      = (cos, sin)(32 theta_f)                   rotation by one tile
+//   tok[t][f]    = (cos, sin)(t theta_f), t < 32            offset inside a tile
+//   start[b][c][f] = (cos, sin)((c * chunk - q_pos[b]) theta_f)   chunk start
+// A lane starts at start (x) tok[l % 32] and advances by `step` per tile.
+struct AngleTables {
+    const float2* step;   // [DH/2]
+    const float2* tok;    // [32][DH/2]
+    const float2* start;  // [B][n_split][DH/2]
+};
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+
+}  // namespace lrkv
