@@ -26,11 +26,17 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INC, "-I" + SRC,
 ]
+# Per-source extras. rope_decode.hip: MFMA accumulators in the arithmetic
+# registers, so that the head-wave kernel's resident Q' (pinned to AGPRs) is read
+# by the MFMAs in place.
+FILE_FLAGS = {
+    "rope_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

@@ -88,6 +88,27 @@ __device__ __forceinline__ float rope_combine(const floatx16& acc, const float* 
     return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
+// Sum of the two half-waves' values (lane l gets v(l) + v(l ^ 32)).
+__device__ __forceinline__ float add_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                    false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// Advance four cos/sin pairs by one tile: (c + i s) * st, written as in-place
+// multiply / multiply-add steps so that the loop-carried values keep their
+// registers.
+__device__ __forceinline__ void rotate4(float* cs, float* sn, const float2* st) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float cy = cs[k] * st[k].y;
+        cs[k] *= st[k].x;
+        cs[k] = fmaf(-sn[k], st[k].y, cs[k]);
+        sn[k] *= st[k].x;
+        sn[k] += cy;
+    }
+}
+
 __device__ void write_empty(float* part, long hstride, int nh, int R, int tid, int nthreads) {
     for (int e = tid; e < nh * (R + 2); e += nthreads) {
         const int h = e / (R + 2), c = e % (R + 2);
@@ -460,6 +481,303 @@ __global__ __launch_bounds__(512, 1) void rope_decode_pp(const RopeArgs p) {
     }
 }
 
+// ============================================================================ head-wave kernel
+// fp16 latents, rank 256, head_dim 128, 4 query heads per unit. One workgroup
+// of 4 waves per (chunk, unit); wave w owns query head w: its Q' (128 x 256
+// fp16, 256 registers per lane) stays resident in the accumulation registers
+// and is read there by the MFMAs, so its scores need no exchange with other
+// waves. Iteration i of the tile loop is one instruction stream:
+//   * RoPE combine of tile i-1's score accumulators (cos/sin per feature);
+//   * tile i's 64 score MFMAs (four 32-row blocks x 16 K steps) in 16 slices,
+//     each slice carrying a share of the vector work: the online softmax of
+//     tile i-1 (p and the rescale factor go to LDS for all waves), the angle
+//     rotation to the next tile, and the value product of tile i-2 for all four
+//     heads on 16x16x32 MFMAs (wave w owns latent dims [64 w, 64 w + 64));
+//   * the loads of tile i+2.
+// A scheduling barrier between slices keeps each share beside its MFMAs, and
+// LDS reads sit at least one slice before their use. One workgroup barrier per
+// tile. Loads go buffer->LDS two tiles ahead (three key and five value buffers;
+// every wave issues exactly 8 loads per tile, so the waits count loads):
+//   keys   rows of 512 B with the 16-byte chunks of row t stored at
+//          chunk ^ (t & 15), so that B-fragment reads (16 lanes = 16 rows, one
+//          chunk) hit distinct banks; one 1 KB load writes two rows; the key
+//          resource ends at the sequence's last token, so rows past it read as
+//          zero (and are masked in the softmax);
+//   values the dim-major 32-token block, with chunk (dim d, tokens 8c..8c+7) of
+//          each 16-dim group stored at 4d + (c ^ s(d)), so that value
+//          A-fragment reads (16 lanes = 16 dims, one token slot) are
+//          conflict-free; tokens past the sequence end are zeroed in registers.
+template <int R>
+__global__ __launch_bounds__(256, 1) void rope_decode_hw(const RopeArgs p) {
+    constexpr int DH = 128, KS = R / 16, RB = DH / 32, NBK = 3, NBV = 5, AH = 2;
+    static_assert(R == 256, "head-wave kernel covers rank 256");
+    __shared__ __attribute__((aligned(1024))) half_t ktile[NBK][32 * R];
+    __shared__ __attribute__((aligned(1024))) half_t vtile[NBV][R * 32];
+    __shared__ __attribute__((aligned(16))) half_t pbuf[2][16][32];   // p of tile j by parity; rows 4.. zero
+    __shared__ float abuf[2][16];                                   // rescale of tile j; entries 4.. one
+    __shared__ float2 stab[RB][2][8];                               // per-tile rotation (row block, half-wave)
+
+    const int g = blockIdx.x;
+    if (g >= p.n_groups) return;
+    const int split = g % p.n_split, u = (g / p.n_split) % p.U, b = g / (p.n_split * p.U);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int Hq = p.U * 4, j = u * 4 + w;
+    const int len = min(p.lens[b], p.cap);
+    const int t_begin = split * p.chunk;
+    const int t_end = min(len, t_begin + p.chunk);
+    const long bu = (long)b * p.U + u;
+    const long hstride = (long)p.n_split * (R + 2);
+    float* part0 = p.part + ((long)(b * Hq + u * 4) * p.n_split + split) * (R + 2);   // head 0 of the unit
+    if (t_begin >= t_end) {
+        write_empty(part0 + w * hstride, 0, 1, R, l, kWave);
+        return;
+    }
+    const int n_tiles = (t_end - t_begin + 31) / 32;
+    const half_t* hk = (const half_t*)p.hk + bu * p.cap * R;
+    const half_t* hv = (const half_t*)p.hv + bu * p.cap * R;      // [cap/32][R][32]
+
+    // value chunk swizzle s(d) for dim d of a 16-dim group: distinct over any 8
+    // (and any 16) consecutive dims of one token slot
+    auto vswz = [](int d) { return (((d >> 1) ^ (d >> 3)) & 1) | (((d >> 2) & 1) << 1); };
+    // lane offsets of the loads: key row 2n + l/32 of the wave's eight, chunk
+    // (l%32) ^ (row & 15); value chunk l of a 1 KB block loads chunk l ^ s(l/4)
+    const uint32_t kx = 512u * (l >> 5) + 16u * ((l & 31) ^ (l >> 5));
+    const uint32_t vx = 16u * (l ^ vswz(l >> 2));
+    // A tile at or past n_tiles gets empty resources: its loads fetch nothing
+    // and write zeros into buffers no longer in use, so that every wave issues
+    // the same number of loads per tile.
+    auto issue_tile = [&](int tile) {
+        const bool real = tile < n_tiles;
+        const int t0 = t_begin + 32 * min(tile, n_tiles - 1), r0 = t0 + 8 * w;
+        const int32x4 kr = make_rsrc(hk + (long)r0 * R, real ? (uint32_t)max(0, len - r0) * (R * 2) : 0u);
+        const half_t* kb = ktile[tile % NBK] + 8 * w * R;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            buf_dma16(kr, (kx ^ (16u * (8 * (w & 1) + 2 * n))) + 1024u * n, kb + 2 * n * R);
+        const int32x4 vr = make_rsrc(hv + (long)(t0 / kTile) * R * kTile + 4 * w * 512, real ? 4096u : 0u);
+        const half_t* vbuf = vtile[tile % NBV] + 4 * w * 512;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) buf_dma16(vr, vx + 1024u * n, vbuf + n * 512);
+    };
+
+    float cs[RB][8], sn[RB][8];
+    {
+        float stc[8], sts[8];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            init_angles(p, b, split, bu, rb, l, DH, cs[rb], sn[rb], stc, sts);
+            if (w == 0 && (l & 31) == 0) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) stab[rb][l >> 5][k] = make_float2(stc[k], sts[k]);
+            }
+        }
+    }
+    // p rows of the padding heads stay zero and their rescale one; the first
+    // loop iteration runs the value product of "tile -1" on a zero p (parity 1)
+    // and the zero-filled value buffer NBV-1, which no load targets before then
+    for (int e = tid; e < 2 * 16 * 32; e += 256) pbuf[e >> 9][(e >> 5) & 15][e & 31] = (half_t)0.0f;
+    if (tid < 32) abuf[tid >> 4][tid & 15] = 1.0f;
+    for (int e = tid; e < R * 32 / 8; e += 256) *reinterpret_cast<half8*>(&vtile[NBV - 1][8 * e]) = half8{};
+    half8 qf[RB][KS];
+    {
+        const half_t* src = p.qp + (((long)b * Hq + j) * DH + (l & 31)) * R + 8 * (l >> 5);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                qf[rb][ks] = *reinterpret_cast<const half8*>(src + (long)32 * rb * R + 16 * ks);
+                // keep Q' in the accumulation registers (AGPRs), read there directly by
+                // the MFMAs as their A operand; the arithmetic registers hold the rest
+                asm volatile("" : "+a"(qf[rb][ks]));
+            }
+    }
+    // B fragment of K step ks: token row l%32, logical chunk 2 ks + l/32, stored at
+    // chunk ^ (row & 15); with ks = 8 m + q that is 16 m + ((2 q + l/32) ^ (row & 15)).
+    int koff[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) koff[q] = (l & 31) * R + 8 * ((2 * q + (l >> 5)) ^ (l & 15));
+    auto kfrag = [&](const half_t* kt, int ks) -> half8 {
+        return *reinterpret_cast<const half8*>(kt + koff[ks & 7] + 128 * (ks >> 3));
+    };
+    // value A fragment of 16-dim group n: dim l%16, token slot l/16
+    const int vro = 8 * (4 * (l & 15) + ((l >> 4) ^ vswz(l & 15)));
+
+    float m_run = -INFINITY, l_acc = 0.0f;
+    floatx4 o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) o[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx16 acc[RB];
+
+    // RoPE combine of row block rb: the lane's 16 features x cos/sin.
+    auto combine = [&](int rb) -> float {
+        float x = 0.0f, y = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+            x = fmaf(cs[rb][k], acc[rb][2 * k], x);
+            x = fmaf(sn[rb][k], acc[rb][2 * k + 1], x);
+            y = fmaf(cs[rb][k + 1], acc[rb][2 * k + 2], y);
+            y = fmaf(sn[rb][k + 1], acc[rb][2 * k + 3], y);
+        }
+        return x + y;
+    };
+    // Online softmax of tile `tile` from the lane's token score: p and the
+    // rescale factor of this head go to LDS for the value product.
+    auto softmax = [&](int tile, float s) {
+        const float mn = fmaxf(m_run, half_max32(s));
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        const float pv = __builtin_amdgcn_exp2f(s - mn);
+        m_run = mn;
+        l_acc = fmaf(l_acc, alpha, pv);
+        pbuf[tile & 1][w][l & 31] = (half_t)pv;
+        abuf[tile & 1][w] = alpha;
+    };
+    // Value product of tile `tile` for all four heads, dims [64 w, 64 w + 64).
+    auto value_product = [&](int tile, bool tail) {
+        const half8 pf = *reinterpret_cast<const half8*>(&pbuf[tile & 1][l & 15][8 * (l >> 4)]);
+        const float al = abuf[tile & 1][l & 15];
+        const half_t* vt = vtile[tile % NBV] + 4 * w * 512 + vro;
+        const int first = t_begin + 32 * tile + 8 * (l >> 4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            half8 a = *reinterpret_cast<const half8*>(vt + 512 * m);
+            if (tail) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (first + e >= len) a[e] = (half_t)0.0f;
+            }
+            o[m] = mfma16(a, pf, o[m] * al);
+        }
+    };
+    auto score_mfma = [&](int tile) {
+        const half_t* kt = ktile[tile % NBK];
+        half8 bq[AH];
+#pragma unroll
+        for (int a = 0; a < AH; ++a) bq[a] = kfrag(kt, a);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const half8 cur = bq[ks % AH];
+            if (ks + AH < KS) bq[ks % AH] = kfrag(kt, ks + AH);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma32(qf[rb][ks], cur, ks == 0 ? floatx16{} : acc[rb]);
+        }
+    };
+
+    // query fragments and angle tables: a real s_waitcnt vmcnt(0), which the
+    // compiler's wait tracking sees, so it adds no waits for them inside the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    issue_tile(0);
+    issue_tile(1);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();
+    issue_tile(2);
+    score_mfma(0);
+    for (int i = 1; i < n_tiles; ++i) {
+        // this wave's loads of tile i are done once at most those of tile i+1 remain
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __syncthreads();
+        float ps[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            ps[rb] = combine(rb);
+            // the first MFMA of block rb (it overwrites acc[rb]) now depends on the
+            // combine, so the accumulator registers are reused in place
+            asm("" : "+a"(qf[rb][0]) : "v"(ps[rb]));
+        }
+        const half_t* kt = ktile[i % NBK];
+        half8 bq[AH];
+#pragma unroll
+        for (int a = 0; a < AH; ++a) bq[a] = kfrag(kt, a);
+        float s = 0.0f, tmax = 0.0f;
+        float2 stv[4];
+        half8 pf = {}, va[2] = {};
+        float al = 1.0f;
+        const int pt = i - 2;                 // -1 at i = 1: zero p, zero values
+        const half_t* vt = vtile[(i + NBV - 2) % NBV] + 4 * w * 512 + vro;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const half8 cur = bq[ks % AH];
+            if (ks + AH < KS) bq[ks % AH] = kfrag(kt, ks + AH);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma32(qf[rb][ks], cur, ks == 0 ? floatx16{} : acc[rb]);
+            // softmax of tile i-1
+            if (ks == 0) {
+                s = add_halves((ps[0] + ps[1]) + (ps[2] + ps[3]));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) stv[k] = stab[0][l >> 5][k];
+            } else if (ks == 1) {
+                tmax = fmaxf(s, dppf<0xB1>(s));
+                tmax = fmaxf(tmax, dppf<0x4E>(tmax));
+            } else if (ks == 2) {
+                tmax = fmaxf(tmax, dppf<0x141>(tmax));
+                tmax = fmaxf(tmax, dppf<0x140>(tmax));
+                tmax = rowpair(tmax, true);
+            } else if (ks == 3) {
+                const float mn = fmaxf(m_run, tmax);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+                const float pv = __builtin_amdgcn_exp2f(s - mn);
+                m_run = mn;
+                l_acc = fmaf(l_acc, alpha, pv);
+                pbuf[(i - 1) & 1][w][l & 31] = (half_t)pv;
+                abuf[(i - 1) & 1][w] = alpha;
+            }
+            // rotation of block (ks-4)/2, half (ks-4)%2, with the step read a slice ahead
+            if (ks >= 4 && ks < 4 + 2 * RB) {
+                const int rb = (ks - 4) >> 1, hf = (ks - 4) & 1;
+                rotate4(cs[rb] + 4 * hf, sn[rb] + 4 * hf, stv);
+                const int nb = (ks - 3) >> 1, nh = (ks - 3) & 1;
+                if (nb < RB) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) stv[k] = stab[nb][l >> 5][4 * nh + k];
+                }
+            }
+            // value product of tile i-2
+            {
+                if (ks == 4) {
+                    pf = *reinterpret_cast<const half8*>(&pbuf[pt & 1][l & 15][8 * (l >> 4)]);
+                    al = abuf[pt & 1][l & 15];
+                }
+                if (ks >= 4 && ks < 8) va[ks & 1] = *reinterpret_cast<const half8*>(vt + 512 * (ks - 4));
+                if (ks >= 5 && ks < 9) {
+                    const int m = ks - 5;
+                    o[m] = mfma16(va[m & 1], pf, o[m] * al);
+                }
+            }
+            // tile i+2's loads go out beside the last MFMAs: its key buffer was last
+            // read by tile i-1's MFMAs and its value buffer by tile i-3's product,
+            // both finished by every wave before this tile's barrier
+            if (ks == KS - 3) issue_tile(i + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmem();                               // the empty loads of tiles n_tiles, n_tiles+1
+    // last tile: combine, masked softmax; then the value products still pending
+    {
+        float ps[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) ps[rb] = combine(rb);
+        float s = add_halves((ps[0] + ps[1]) + (ps[2] + ps[3]));
+        if (t_begin + 32 * (n_tiles - 1) + (l & 31) >= len) s = -INFINITY;
+        softmax(n_tiles - 1, s);
+    }
+    __syncthreads();
+    if (n_tiles >= 2) value_product(n_tiles - 2, false);
+    value_product(n_tiles - 1, true);
+
+    // lanes with head l%16 < 4 hold dims 16 (4 w + m) + 4 (l/16) + e of that head
+    if ((l & 15) < 4) {
+        float* ph = part0 + (l & 15) * hstride + 2 + 64 * w + 4 * (l >> 4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ph[16 * m + e] = o[m][e];
+    }
+    const float lsum = half_sum32(l_acc);
+    if (l == 0) {
+        part0[w * hstride + 0] = m_run;
+        part0[w * hstride + 1] = lsum;
+    }
+}
+
 template <int R, int DH, int NHW, bool INT4>
 void launch_generic(RopeArgs a, hipStream_t st) {
     a.n_groups = a.n_split * a.U * a.B;
@@ -484,7 +802,7 @@ int32_t launch_rope_decode(const lrkv_latent_cache* c, const half_t* qp, const f
                c->units, nh, c->capacity, n_split, chunk, 0};
     if (r == 256 && dh == 128 && nh == 4 && !int4) {
         a.n_groups = n_split * a.U * a.B;
-        hipLaunchKernelGGL(rope_decode_pp<256>, dim3(a.n_groups), dim3(512), 0, st, a);
+        hipLaunchKernelGGL(rope_decode_hw<256>, dim3(a.n_groups), dim3(256), 0, st, a);
         return LRKV_OK;
     }
     // heads per workgroup of the generic kernel: two for the larger ranks

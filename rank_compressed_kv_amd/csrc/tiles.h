@@ -57,6 +57,29 @@ __device__ __forceinline__ void dma16_async(const void* src, const void* dst) {
                  :: "s"(lds), "v"(src) : "memory", "m0");
 }
 
+// Raw buffer resource over [base, base + bytes): loads at or past `bytes` read
+// as zero. Word 3 is the gfx9 raw 32-bit data format. Built from wave-uniform
+// values, held in scalar registers.
+typedef int32_t int32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    int32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((a >> 32) & 0xffffu));   // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+// buffer_load_dwordx4 ... lds as inline assembly (so the compiler adds no waits
+// before LDS reads; the caller counts vmcnt): lane i loads 16 bytes at
+// base + voff and writes them to LDS at lds + 16 i. `rsrc` and `lds` must be
+// wave-uniform. No immediate or scalar offset (zero on this path).
+__device__ __forceinline__ void buf_dma16(int32x4 rsrc, uint32_t voff, const void* lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(m) : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- key tile, register staging
 // 32 tokens x R fp16 rows in LDS with rows padded to R + 8 halves; int4 codes are
 // dequantised on the way (code * scale rounded to fp16). Rows at or past t_end
