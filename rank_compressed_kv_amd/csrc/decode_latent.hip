@@ -5,10 +5,12 @@
 namespace lrkv {
 
 bool rope_shape_supported(int r, int dh, int nh);
+bool rope_fragment_layout(const lrkv_latent_cache* c);
 bool absorbed_shape_supported(int r, int nh);
 void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, const int32_t* lens,
                       half_t* qp, float* qs, float2* angles, int B, int U, int s, int gq, int DH,
-                      int R, int n_split, int chunk, double theta, float scale, hipStream_t st);
+                      int R, int n_split, int chunk, double theta, float scale, bool frag,
+                      hipStream_t st);
 int32_t launch_rope_decode(const lrkv_latent_cache* c, const half_t* qp, const float* qs,
                            const float2* angles, float* part, int n_split, int chunk, hipStream_t st);
 int32_t launch_absorbed_decode(const lrkv_latent_cache* c, const float* q, float* part, int n_split,
@@ -33,7 +35,8 @@ int32_t launch_decode_latent(int mode, int phases, const lrkv_latent_cache* c, c
         float2* angles = (float2*)(base + w.ang_off);
         if (phases & kPhasePrepare)
             launch_rope_prep(q, bk, q_pos, c->lens, qp, qs, angles, g.B, g.U, g.s, g.gq, g.dh, g.r,
-                             w.n_split, w.chunk, (double)g.theta, sm_scale * kLog2e, st);
+                             w.n_split, w.chunk, (double)g.theta, sm_scale * kLog2e,
+                             rope_fragment_layout(c), st);
         if (phases & kPhasePartials) {
             const int32_t rc = launch_rope_decode(c, qp, qs, angles, part, w.n_split, w.chunk, st);
             if (rc != LRKV_OK) return rc;

@@ -481,23 +481,29 @@ __global__ __launch_bounds__(512, 1) void rope_decode_pp(const RopeArgs p) {
     }
 }
 
-// ============================================================================ head-wave kernel
+// ============================================================================ frequency-wave kernel
 // fp16 latents, rank 256, head_dim 128, 4 query heads per unit. One workgroup
-// of 4 waves per (chunk, unit); wave w owns query head w: its Q' (128 x 256
-// fp16, 256 registers per lane) stays resident in the accumulation registers
-// and is read there by the MFMAs, so its scores need no exchange with other
-// waves. Iteration i of the tile loop is one instruction stream:
-//   * RoPE combine of tile i-1's score accumulators (cos/sin per feature);
-//   * tile i's 64 score MFMAs (four 32-row blocks x 16 K steps) in 16 slices,
-//     each slice carrying a share of the vector work: the online softmax of
-//     tile i-1 (p and the rescale factor go to LDS for all waves), the angle
-//     rotation to the next tile, and the value product of tile i-2 for all four
-//     heads on 16x16x32 MFMAs (wave w owns latent dims [64 w, 64 w + 64));
-//   * the loads of tile i+2.
+// of 4 waves per (chunk, unit). Wave w owns feature rows [32 w, 32 w + 32) of
+// every head's Q' (frequencies 16 w .. 16 w + 15): 4 heads x 32 rows x 256 fp16
+// = 256 registers per lane, resident in the accumulation registers and read
+// there by the MFMAs. A lane's eight cos/sin pairs (its token, its
+// frequencies) serve all four heads, so the per-tile angle rotation is shared.
+// Iteration i of the tile loop is one instruction stream:
+//   * RoPE combine of tile i-1's accumulators into per-wave partial scores,
+//     which go to LDS;
+//   * tile i's 64 score MFMAs (4 heads x 16 K steps) in 16 slices, each slice
+//     carrying a share of the vector work: the softmax of tile i-2 for head w
+//     (sum of the four waves' partials; p and the rescale factor to LDS), the
+//     angle rotation, and the value product of tile i-3 for all four heads on
+//     16x16x32 MFMAs (wave w owns latent dims [64 w, 64 w + 64));
+//   * the loads of tile i+3's keys and tile i+1's values.
 // A scheduling barrier between slices keeps each share beside its MFMAs, and
 // LDS reads sit at least one slice before their use. One workgroup barrier per
-// tile. Loads go buffer->LDS two tiles ahead (three key and five value buffers;
-// every wave issues exactly 8 loads per tile, so the waits count loads):
+// tile; the stages that exchange data run one tile apart, so that barrier
+// orders every exchange. Loads go buffer->LDS, keys three tiles ahead (four
+// buffers) and values one tile ahead of tile i (five buffers: the value product
+// lags three tiles); every wave issues exactly 8 loads per tile, so the waits
+// count loads:
 //   keys   rows of 512 B with the 16-byte chunks of row t stored at
 //          chunk ^ (t & 15), so that B-fragment reads (16 lanes = 16 rows, one
 //          chunk) hit distinct banks; one 1 KB load writes two rows; the key
@@ -507,27 +513,31 @@ __global__ __launch_bounds__(512, 1) void rope_decode_pp(const RopeArgs p) {
 //          each 16-dim group stored at 4d + (c ^ s(d)), so that value
 //          A-fragment reads (16 lanes = 16 dims, one token slot) are
 //          conflict-free; tokens past the sequence end are zeroed in registers.
+// The first iterations run the softmax and value product of tiles -2 and -1
+// on prepared no-op data (scores -inf, p zero, rescale one, values zero).
 template <int R>
-__global__ __launch_bounds__(256, 1) void rope_decode_hw(const RopeArgs p) {
-    constexpr int DH = 128, KS = R / 16, RB = DH / 32, NBK = 3, NBV = 5, AH = 2;
-    static_assert(R == 256, "head-wave kernel covers rank 256");
+__global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
+    constexpr int DH = 128, KS = R / 16, NH = 4, NBK = 4, NBV = 5, AH = 2;
+    static_assert(R == 256, "frequency-wave kernel covers rank 256");
     __shared__ __attribute__((aligned(1024))) half_t ktile[NBK][32 * R];
     __shared__ __attribute__((aligned(1024))) half_t vtile[NBV][R * 32];
-    __shared__ __attribute__((aligned(16))) half_t pbuf[2][16][32];   // p of tile j by parity; rows 4.. zero
-    __shared__ float abuf[2][16];                                   // rescale of tile j; entries 4.. one
-    __shared__ float2 stab[RB][2][8];                               // per-tile rotation (row block, half-wave)
+    __shared__ __attribute__((aligned(16))) float sbuf[2][NH][4][32];  // partial scores [tile parity][head][wave][token]
+    __shared__ __attribute__((aligned(16))) half_t pbuf[2][16][32];    // p [tile parity][head][token]; rows 4.. zero
+    __shared__ float abuf[2][16];                                      // rescale [tile parity][head]; entries 4.. one
 
+    // unit-minor block order: blocks are dealt to the XCDs round-robin, so with 8
+    // units each XCD runs every chunk of one unit and its L2 holds that unit's Q'
     const int g = blockIdx.x;
     if (g >= p.n_groups) return;
-    const int split = g % p.n_split, u = (g / p.n_split) % p.U, b = g / (p.n_split * p.U);
+    const int u = g % p.U, split = (g / p.U) % p.n_split, b = g / (p.n_split * p.U);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int Hq = p.U * 4, j = u * 4 + w;
+    const int Hq = p.U * NH;
     const int len = min(p.lens[b], p.cap);
     const int t_begin = split * p.chunk;
     const int t_end = min(len, t_begin + p.chunk);
     const long bu = (long)b * p.U + u;
     const long hstride = (long)p.n_split * (R + 2);
-    float* part0 = p.part + ((long)(b * Hq + u * 4) * p.n_split + split) * (R + 2);   // head 0 of the unit
+    float* part0 = p.part + ((long)(b * Hq + u * NH) * p.n_split + split) * (R + 2);   // head 0 of the unit
     if (t_begin >= t_end) {
         write_empty(part0 + w * hstride, 0, 1, R, l, kWave);
         return;
@@ -544,53 +554,62 @@ __global__ __launch_bounds__(256, 1) void rope_decode_hw(const RopeArgs p) {
     const uint32_t kx = 512u * (l >> 5) + 16u * ((l & 31) ^ (l >> 5));
     const uint32_t vx = 16u * (l ^ vswz(l >> 2));
     // A tile at or past n_tiles gets empty resources: its loads fetch nothing
-    // and write zeros into buffers no longer in use, so that every wave issues
-    // the same number of loads per tile.
-    auto issue_tile = [&](int tile) {
+    // and write zeros into buffers no longer in use. Each call is 4 loads.
+    auto issue_keys = [&](int tile) {
         const bool real = tile < n_tiles;
-        const int t0 = t_begin + 32 * min(tile, n_tiles - 1), r0 = t0 + 8 * w;
+        const int r0 = t_begin + 32 * min(tile, n_tiles - 1) + 8 * w;
         const int32x4 kr = make_rsrc(hk + (long)r0 * R, real ? (uint32_t)max(0, len - r0) * (R * 2) : 0u);
         const half_t* kb = ktile[tile % NBK] + 8 * w * R;
 #pragma unroll
         for (int n = 0; n < 4; ++n)
             buf_dma16(kr, (kx ^ (16u * (8 * (w & 1) + 2 * n))) + 1024u * n, kb + 2 * n * R);
+    };
+    auto issue_values = [&](int tile) {
+        const bool real = tile < n_tiles;
+        const int t0 = t_begin + 32 * min(tile, n_tiles - 1);
         const int32x4 vr = make_rsrc(hv + (long)(t0 / kTile) * R * kTile + 4 * w * 512, real ? 4096u : 0u);
         const half_t* vbuf = vtile[tile % NBV] + 4 * w * 512;
 #pragma unroll
         for (int n = 0; n < 4; ++n) buf_dma16(vr, vx + 1024u * n, vbuf + n * 512);
     };
 
-    float cs[RB][8], sn[RB][8];
+    // Everything the loop starts from is requested at once: the first key and
+    // value tiles, Q' and the angle tables (one wait below). Load order: keys 0,
+    // values 0, keys 1, keys 2; then in iteration j (j = 0 in the prologue) keys
+    // j+3 and values j+1. Keys of tile i are waited for at the top of iteration
+    // i: the loads issued after them are then at most 12, 16 and from i = 3 on
+    // 20 (values i-2 and the two following iterations).
+    issue_keys(0);
+    issue_values(0);
+    issue_keys(1);
+    issue_keys(2);
+    half8 qf[NH][KS];
+    {
+        // fragment-major Q': one contiguous 1 KB block per (row block, head, K step),
+        // loaded into the accumulation registers (AGPRs), where the MFMAs read it
+        // as their A operand
+        const half_t* src = p.qp + ((bu * (DH / 32) + w) * NH * KS) * 512 + 8 * l;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qf[h][ks] = *reinterpret_cast<const half8*>(src + (h * KS + ks) * 512);
+    }
+    // cos/sin (with the frequency's 2^-e) of the lane's token and eight
+    // frequencies in the first tile, and the rotation by one tile
+    float cs[8], sn[8];
+    float2 stp[8];
     {
         float stc[8], sts[8];
+        init_angles(p, b, split, bu, w, l, DH, cs, sn, stc, sts);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            init_angles(p, b, split, bu, rb, l, DH, cs[rb], sn[rb], stc, sts);
-            if (w == 0 && (l & 31) == 0) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) stab[rb][l >> 5][k] = make_float2(stc[k], sts[k]);
-            }
-        }
+        for (int k = 0; k < 8; ++k) stp[k] = make_float2(stc[k], sts[k]);
     }
-    // p rows of the padding heads stay zero and their rescale one; the first
-    // loop iteration runs the value product of "tile -1" on a zero p (parity 1)
-    // and the zero-filled value buffer NBV-1, which no load targets before then
+    // no-op data for tiles -2 and -1 (see above)
+    for (int e = tid; e < NH * 4 * 32; e += 256) (&sbuf[1][0][0][0])[e] = -INFINITY;
     for (int e = tid; e < 2 * 16 * 32; e += 256) pbuf[e >> 9][(e >> 5) & 15][e & 31] = (half_t)0.0f;
     if (tid < 32) abuf[tid >> 4][tid & 15] = 1.0f;
-    for (int e = tid; e < R * 32 / 8; e += 256) *reinterpret_cast<half8*>(&vtile[NBV - 1][8 * e]) = half8{};
-    half8 qf[RB][KS];
-    {
-        const half_t* src = p.qp + (((long)b * Hq + j) * DH + (l & 31)) * R + 8 * (l >> 5);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qf[rb][ks] = *reinterpret_cast<const half8*>(src + (long)32 * rb * R + 16 * ks);
-                // keep Q' in the accumulation registers (AGPRs), read there directly by
-                // the MFMAs as their A operand; the arithmetic registers hold the rest
-                asm volatile("" : "+a"(qf[rb][ks]));
-            }
-    }
+    for (int e = tid; e < 2 * R * 32 / 8; e += 256)
+        *reinterpret_cast<half8*>(&vtile[NBV - 2][8 * e]) = half8{};   // buffers NBV-2 and NBV-1
     // B fragment of K step ks: token row l%32, logical chunk 2 ks + l/32, stored at
     // chunk ^ (row & 15); with ks = 8 m + q that is 16 m + ((2 q + l/32) ^ (row & 15)).
     int koff[8];
@@ -599,43 +618,48 @@ __global__ __launch_bounds__(256, 1) void rope_decode_hw(const RopeArgs p) {
     auto kfrag = [&](const half_t* kt, int ks) -> half8 {
         return *reinterpret_cast<const half8*>(kt + koff[ks & 7] + 128 * (ks >> 3));
     };
-    // value A fragment of 16-dim group n: dim l%16, token slot l/16
+    // value A fragment of a 16-dim group: dim l%16, token slot l/16
     const int vro = 8 * (4 * (l & 15) + ((l >> 4) ^ vswz(l & 15)));
 
     float m_run = -INFINITY, l_acc = 0.0f;
     floatx4 o[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) o[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    floatx16 acc[RB];
+    floatx16 acc[NH];
 
-    // RoPE combine of row block rb: the lane's 16 features x cos/sin.
-    auto combine = [&](int rb) -> float {
+    // RoPE combine of head h: the lane's 16 features x cos/sin.
+    auto combine = [&](int h) -> float {
         float x = 0.0f, y = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
-            x = fmaf(cs[rb][k], acc[rb][2 * k], x);
-            x = fmaf(sn[rb][k], acc[rb][2 * k + 1], x);
-            y = fmaf(cs[rb][k + 1], acc[rb][2 * k + 2], y);
-            y = fmaf(sn[rb][k + 1], acc[rb][2 * k + 3], y);
+            x = fmaf(cs[k], acc[h][2 * k], x);
+            x = fmaf(sn[k], acc[h][2 * k + 1], x);
+            y = fmaf(cs[k + 1], acc[h][2 * k + 2], y);
+            y = fmaf(sn[k + 1], acc[h][2 * k + 3], y);
         }
         return x + y;
     };
-    // Online softmax of tile `tile` from the lane's token score: p and the
-    // rescale factor of this head go to LDS for the value product.
-    auto softmax = [&](int tile, float s) {
-        const float mn = fmaxf(m_run, half_max32(s));
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        const float pv = __builtin_amdgcn_exp2f(s - mn);
+    // Online-softmax update of head w from the tile's token scores (the sum of
+    // the four waves' partials); p and the rescale factor go to LDS. A tile of
+    // -inf scores (the no-op tiles) leaves the state as it is.
+    auto softmax_update = [&](int tile, float s, float tmax) {
+        const float mn = fmaxf(m_run, tmax);
+        const float alpha = mn == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
+        const float pv = s == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s - mn);
         m_run = mn;
         l_acc = fmaf(l_acc, alpha, pv);
         pbuf[tile & 1][w][l & 31] = (half_t)pv;
         abuf[tile & 1][w] = alpha;
     };
+    auto read_scores = [&](int tile) -> float {
+        const float* sp = &sbuf[tile & 1][w][0][l & 31];
+        return (sp[0] + sp[32]) + (sp[64] + sp[96]);
+    };
     // Value product of tile `tile` for all four heads, dims [64 w, 64 w + 64).
     auto value_product = [&](int tile, bool tail) {
         const half8 pf = *reinterpret_cast<const half8*>(&pbuf[tile & 1][l & 15][8 * (l >> 4)]);
         const float al = abuf[tile & 1][l & 15];
-        const half_t* vt = vtile[tile % NBV] + 4 * w * 512 + vro;
+        const half_t* vt = vtile[(tile + NBV) % NBV] + 4 * w * 512 + vro;
         const int first = t_begin + 32 * tile + 8 * (l >> 4);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -648,6 +672,15 @@ __global__ __launch_bounds__(256, 1) void rope_decode_hw(const RopeArgs p) {
             o[m] = mfma16(a, pf, o[m] * al);
         }
     };
+    // Partial scores of tile `tile` (this wave's frequencies) to LDS.
+    auto write_partials = [&](int tile, const float* ps, bool tail) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            float v = add_halves(ps[h]);
+            if (tail && t_begin + 32 * tile + (l & 31) >= len) v = -INFINITY;
+            sbuf[tile & 1][h][w][l & 31] = v;
+        }
+    };
     auto score_mfma = [&](int tile) {
         const half_t* kt = ktile[tile % NBK];
         half8 bq[AH];
@@ -658,52 +691,54 @@ __global__ __launch_bounds__(256, 1) void rope_decode_hw(const RopeArgs p) {
             const half8 cur = bq[ks % AH];
             if (ks + AH < KS) bq[ks % AH] = kfrag(kt, ks + AH);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma32(qf[rb][ks], cur, ks == 0 ? floatx16{} : acc[rb]);
+            for (int h = 0; h < NH; ++h) acc[h] = mfma32(qf[h][ks], cur, ks == 0 ? floatx16{} : acc[h]);
         }
     };
 
-    // query fragments and angle tables: a real s_waitcnt vmcnt(0), which the
-    // compiler's wait tracking sees, so it adds no waits for them inside the loop
+    // the one wait: a real s_waitcnt vmcnt(0), which the compiler's wait tracking
+    // sees, so it adds no waits for these loads inside the loop. Q' is pinned to
+    // the AGPRs only now: pinning a fragment right after its own load would
+    // serialize the round trips.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    issue_tile(0);
-    issue_tile(1);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[h][ks]));
     __syncthreads();
-    issue_tile(2);
+    issue_keys(3);
+    issue_values(1);
     score_mfma(0);
     for (int i = 1; i < n_tiles; ++i) {
-        // this wave's loads of tile i are done once at most those of tile i+1 remain
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        if (i >= 3) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+        else if (i == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
         __syncthreads();
-        float ps[RB];
+        float ps[NH];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            ps[rb] = combine(rb);
-            // the first MFMA of block rb (it overwrites acc[rb]) now depends on the
+        for (int h = 0; h < NH; ++h) {
+            ps[h] = combine(h);
+            // the first MFMA of head h (it overwrites acc[h]) now depends on the
             // combine, so the accumulator registers are reused in place
-            asm("" : "+a"(qf[rb][0]) : "v"(ps[rb]));
+            asm("" : "+a"(qf[h][0]) : "v"(ps[h]));
         }
         const half_t* kt = ktile[i % NBK];
         half8 bq[AH];
 #pragma unroll
         for (int a = 0; a < AH; ++a) bq[a] = kfrag(kt, a);
         float s = 0.0f, tmax = 0.0f;
-        float2 stv[4];
         half8 pf = {}, va[2] = {};
         float al = 1.0f;
-        const int pt = i - 2;                 // -1 at i = 1: zero p, zero values
-        const half_t* vt = vtile[(i + NBV - 2) % NBV] + 4 * w * 512 + vro;
+        const int st = i - 2, vt_tile = i - 3;   // softmax / value-product tiles (negative: no-op data)
+        const half_t* vt = vtile[(vt_tile + NBV) % NBV] + 4 * w * 512 + vro;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const half8 cur = bq[ks % AH];
             if (ks + AH < KS) bq[ks % AH] = kfrag(kt, ks + AH);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma32(qf[rb][ks], cur, ks == 0 ? floatx16{} : acc[rb]);
-            // softmax of tile i-1
+            for (int h = 0; h < NH; ++h) acc[h] = mfma32(qf[h][ks], cur, ks == 0 ? floatx16{} : acc[h]);
             if (ks == 0) {
-                s = add_halves((ps[0] + ps[1]) + (ps[2] + ps[3]));
-#pragma unroll
-                for (int k = 0; k < 4; ++k) stv[k] = stab[0][l >> 5][k];
+                write_partials(i - 1, ps, false);
+                s = read_scores(st);
             } else if (ks == 1) {
                 tmax = fmaxf(s, dppf<0xB1>(s));
                 tmax = fmaxf(tmax, dppf<0x4E>(tmax));
@@ -712,59 +747,54 @@ __global__ __launch_bounds__(256, 1) void rope_decode_hw(const RopeArgs p) {
                 tmax = fmaxf(tmax, dppf<0x140>(tmax));
                 tmax = rowpair(tmax, true);
             } else if (ks == 3) {
-                const float mn = fmaxf(m_run, tmax);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-                const float pv = __builtin_amdgcn_exp2f(s - mn);
-                m_run = mn;
-                l_acc = fmaf(l_acc, alpha, pv);
-                pbuf[(i - 1) & 1][w][l & 31] = (half_t)pv;
-                abuf[(i - 1) & 1][w] = alpha;
+                softmax_update(st, s, tmax);
+            } else if (ks == 4 || ks == 5) {
+                rotate4(cs + 4 * (ks - 4), sn + 4 * (ks - 4), stp + 4 * (ks - 4));
             }
-            // rotation of block (ks-4)/2, half (ks-4)%2, with the step read a slice ahead
-            if (ks >= 4 && ks < 4 + 2 * RB) {
-                const int rb = (ks - 4) >> 1, hf = (ks - 4) & 1;
-                rotate4(cs[rb] + 4 * hf, sn[rb] + 4 * hf, stv);
-                const int nb = (ks - 3) >> 1, nh = (ks - 3) & 1;
-                if (nb < RB) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) stv[k] = stab[nb][l >> 5][4 * nh + k];
-                }
+            // value product of tile i-3
+            if (ks == 6) {
+                pf = *reinterpret_cast<const half8*>(&pbuf[vt_tile & 1][l & 15][8 * (l >> 4)]);
+                al = abuf[vt_tile & 1][l & 15];
             }
-            // value product of tile i-2
-            {
-                if (ks == 4) {
-                    pf = *reinterpret_cast<const half8*>(&pbuf[pt & 1][l & 15][8 * (l >> 4)]);
-                    al = abuf[pt & 1][l & 15];
-                }
-                if (ks >= 4 && ks < 8) va[ks & 1] = *reinterpret_cast<const half8*>(vt + 512 * (ks - 4));
-                if (ks >= 5 && ks < 9) {
-                    const int m = ks - 5;
-                    o[m] = mfma16(va[m & 1], pf, o[m] * al);
-                }
+            if (ks >= 6 && ks < 10) va[ks & 1] = *reinterpret_cast<const half8*>(vt + 512 * (ks - 6));
+            if (ks >= 7 && ks < 11) {
+                const int m = ks - 7;
+                o[m] = mfma16(va[m & 1], pf, o[m] * al);
             }
-            // tile i+2's loads go out beside the last MFMAs: its key buffer was last
-            // read by tile i-1's MFMAs and its value buffer by tile i-3's product,
-            // both finished by every wave before this tile's barrier
-            if (ks == KS - 3) issue_tile(i + 2);
+            // keys of tile i+3 (their buffer was last read by tile i-1's MFMAs) and
+            // values of tile i+1 (buffer last read by tile i-4's product), both
+            // finished by every wave before this tile's barrier
+            if (ks == 1) issue_keys(i + 3);
+            if (ks == 2) issue_values(i + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    wait_vmem();                               // the empty loads of tiles n_tiles, n_tiles+1
-    // last tile: combine, masked softmax; then the value products still pending
+    wait_vmem();                               // the loads past the last tile (empty)
+    // drain: partials of the last tile; softmax of the last two tiles; value
+    // products of the last three, each exchange separated by a barrier
     {
-        float ps[RB];
+        float ps[NH];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) ps[rb] = combine(rb);
-        float s = add_halves((ps[0] + ps[1]) + (ps[2] + ps[3]));
-        if (t_begin + 32 * (n_tiles - 1) + (l & 31) >= len) s = -INFINITY;
-        softmax(n_tiles - 1, s);
+        for (int h = 0; h < NH; ++h) ps[h] = combine(h);
+        write_partials(n_tiles - 1, ps, true);
     }
     __syncthreads();
-    if (n_tiles >= 2) value_product(n_tiles - 2, false);
+    {
+        const float s = read_scores(n_tiles - 2);
+        softmax_update(n_tiles - 2, s, half_max32(s));
+    }
+    value_product(n_tiles - 3, false);
+    __syncthreads();
+    {
+        const float s = read_scores(n_tiles - 1);
+        softmax_update(n_tiles - 1, s, half_max32(s));
+    }
+    __syncthreads();
+    value_product(n_tiles - 2, false);
     value_product(n_tiles - 1, true);
 
     // lanes with head l%16 < 4 hold dims 16 (4 w + m) + 4 (l/16) + e of that head
-    if ((l & 15) < 4) {
+    if ((l & 15) < NH) {
         float* ph = part0 + (l & 15) * hstride + 2 + 64 * w + 4 * (l >> 4);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -787,6 +817,15 @@ void launch_generic(RopeArgs a, hipStream_t st) {
 
 }  // namespace
 
+// The frequency-wave kernel: fp16 rank-256 units of four 128-dim heads, with
+// 32-bit byte offsets into one unit's cache. Its queries are prepared in
+// fragment order.
+static bool use_frequency_wave(const lrkv_latent_cache* c) {
+    return c->rank == 256 && c->head_dim == 128 && c->kv_per_unit * c->q_per_kv == 4 &&
+           c->fmt == LRKV_FMT_FP16 && (size_t)c->capacity * 256 * 2 < ((size_t)1 << 32);
+}
+bool rope_fragment_layout(const lrkv_latent_cache* c) { return use_frequency_wave(c); }
+
 bool rope_shape_supported(int r, int dh, int nh) {
     return (r == 32 && dh == 64 && nh == 2) || (r == 64 && dh == 64 && nh == 2) ||
            (r == 256 && dh == 128 && nh == 4) || (r == 64 && dh == 128 && nh == 4) ||
@@ -800,9 +839,9 @@ int32_t launch_rope_decode(const lrkv_latent_cache* c, const half_t* qp, const f
     RopeArgs a{c->hk, c->hv, (const half_t*)c->sk, (const half_t*)c->sv, c->lens, qp, qs,
                AngleTables{angles, angles + dh / 2, angles + 33 * (dh / 2)}, part, c->batch,
                c->units, nh, c->capacity, n_split, chunk, 0};
-    if (r == 256 && dh == 128 && nh == 4 && !int4) {
+    if (use_frequency_wave(c)) {
         a.n_groups = n_split * a.U * a.B;
-        hipLaunchKernelGGL(rope_decode_hw<256>, dim3(a.n_groups), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(rope_decode_fw<256>, dim3(a.n_groups), dim3(256), 0, st, a);
         return LRKV_OK;
     }
     // heads per workgroup of the generic kernel: two for the larger ranks

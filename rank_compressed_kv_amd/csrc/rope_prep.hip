@@ -9,6 +9,11 @@
 //     u_i = q_i B[:, i] + q_{i+h} B[:, i+h],   w_i = q_{i+h} B[:, i] - q_i B[:, i+h]
 // This step writes Q' = [u_0, w_0, u_1, w_1, ...] (d_h rows of r values, fp16)
 // for every head, and the cos/sin tables of the phi_i (fp64 angles, fp32 values).
+// Q' is stored row-major per head, or (for the rank-256, d_h-128, 4-head units
+// of the frequency-wave kernel) in MFMA-fragment order: for unit (b, u), row
+// block w (rows 32 w .. 32 w + 31), head h and K step ks, one contiguous 1 KB
+// block whose 16 bytes at 16 l are the A fragment of lane l (row 32 w + l%32,
+// columns 16 ks + 8 (l/32) .. + 7).
 #include "common.h"
 
 #include <math.h>
@@ -23,10 +28,16 @@ constexpr double kTwoPi = 6.283185307179586476925286766559;
 // frequency lands in [2^14, 2^15) (fp16 range). 2^-e_i goes to qs.
 // Grid: (B*U, DH/8); block: 4 frequencies; the 8 needed B columns of every
 // head are staged in LDS with 8-byte loads first.
+__device__ __forceinline__ size_t qp_index(bool frag, int bu, int NH, int h, int DH, int R, int row, int k) {
+    if (!frag) return ((size_t)bu * NH + h) * DH * R + (size_t)row * R + k;
+    const int w = row >> 5, ks = k >> 4, lane = (row & 31) + 32 * ((k >> 3) & 1);
+    return ((((size_t)bu * (DH / 32) + w) * NH + h) * (R / 16) + ks) * 512 + lane * 8 + (k & 7);
+}
 __global__ __launch_bounds__(256) void rope_qprep(const float* __restrict__ q,
                                                   const half_t* __restrict__ bk,
                                                   half_t* __restrict__ qp, float* __restrict__ qs,
-                                                  int U, int s, int gq, int DH, int R, float scale) {
+                                                  int U, int s, int gq, int DH, int R, float scale,
+                                                  bool frag) {
     constexpr int MAXR = 256, MAXNH = 8;
     __shared__ __attribute__((aligned(8))) half_t Bs[MAXNH][2][MAXR][4];
     __shared__ float red[4][4];
@@ -64,11 +75,10 @@ __global__ __launch_bounds__(256) void rope_qprep(const float* __restrict__ q,
         const int j = u * NH + h;
         const float qa = ldexpf(q[((size_t)b * Hq + j) * DH + i] * scale, ex);
         const float qb = ldexpf(q[((size_t)b * Hq + j) * DH + i + half] * scale, ex);
-        half_t* out = qp + ((size_t)b * Hq + j) * DH * R;
         for (int k = kl; k < R; k += 64) {
             const float b0 = (float)Bs[h][0][k][fi], b1 = (float)Bs[h][1][k][fi];
-            out[(size_t)(2 * i) * R + k] = (half_t)fmaf(qa, b0, qb * b1);
-            out[(size_t)(2 * i + 1) * R + k] = (half_t)fmaf(qb, b0, -qa * b1);
+            qp[qp_index(frag, bu, NH, h, DH, R, 2 * i, k)] = (half_t)fmaf(qa, b0, qb * b1);
+            qp[qp_index(frag, bu, NH, h, DH, R, 2 * i + 1, k)] = (half_t)fmaf(qb, b0, -qa * b1);
         }
     }
     if (kl == 0) qs[((size_t)b * U + u) * half + i] = ldexpf(1.0f, -ex);
@@ -109,9 +119,10 @@ __global__ __launch_bounds__(256) void rope_angles(float2* __restrict__ tab,
 
 void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, const int32_t* lens,
                       half_t* qp, float* qs, float2* angles, int B, int U, int s, int gq, int DH,
-                      int R, int n_split, int chunk, double theta, float scale, hipStream_t st) {
+                      int R, int n_split, int chunk, double theta, float scale, bool frag,
+                      hipStream_t st) {
     hipLaunchKernelGGL(rope_qprep, dim3(B * U, DH / 8), dim3(256), 0, st, q, bk, qp, qs, U, s, gq, DH,
-                       R, scale);
+                       R, scale, frag);
     const int n = (33 + B * n_split) * (DH / 2);
     hipLaunchKernelGGL(rope_angles, dim3((n + 255) / 256), dim3(256), 0, st, angles, q_pos, lens, B,
                        n_split, chunk, DH / 2, theta);
