@@ -15,7 +15,10 @@ Inputs are resident in HBM before the timed region. Two cache replicas are
 used in turn so that consecutive steps do not re-read the same 537 MB from the
 256 MB last-level cache.
 
-Prints one JSON line (see the repository's design doc for the fields).
+Prints one JSON line: the metric, whole-step throughput (latent-cache bytes per
+second over the timed steps), the partials kernel's achieved bandwidth against
+the HBM peak (roofline), and the float64 oracle timed on the host
+(cpu_baseline).
 """
 from __future__ import annotations
 
@@ -43,6 +46,28 @@ FLOP_PER_UNIT_TOKEN = 2 * R * S * DH + 2 * S * DH + 2 * S * R
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "rank_compressed_kv_amd", "csrc", "rope_decode.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "rope_decode_fw_llama2_7b_T65536.md")
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the partials kernel from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the kernel
+    source has changed since they were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_RECORD).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != src:
+        return None
+    return float(t.group(1))
 
 
 def cpu_baseline(T: int, budget_s: float = 12.0) -> dict:
@@ -86,9 +111,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the decode shards by unit, batch or sequence chunk with no exchange "
-              "except a partial-state all-gather; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU and has no multi-GPU path (the decode would "
+              "shard by unit, batch or sequence chunk, exchanging only the per-chunk "
+              "partial states before the merge)", file=sys.stderr)
         return 2
 
     import torch
@@ -98,9 +123,9 @@ def main() -> int:
 
     lrkv.load_library()
     dev = torch.device("cuda:0")
-    T, K, W, NR = args.T, args.steps, args.warmup, max(1, args.replicas)
+    T, K, W, NR, D = args.T, args.steps, args.warmup, max(1, args.replicas), 8
     T_init = T - 1 - W // NR
-    cap = ((T + K + W + 64) // 32) * 32
+    cap = ((T + K + W + D + 64) // 32) * 32
 
     log(f"bench: generating latents for T={T_init} (B={B}, U={U}, r={R})")
     lay = synth.latent_layer(2, B, U, T_init, R, S * DH, TAU)
@@ -114,18 +139,18 @@ def main() -> int:
         c.append(hk0, hv0)
         reps.append(c)
     del hk0, hv0
-    step_tok = synth.latent_layer(3, B, U, W + K, R, S * DH, TAU)
+    step_tok = synth.latent_layer(3, B, U, W + K + D, R, S * DH, TAU)
     nk = torch.from_numpy(step_tok["hk"]).to(dev)
     nv = torch.from_numpy(step_tok["hv"]).to(dev)
-    new_k = [nk[:, :, i:i + 1].contiguous() for i in range(W + K)]
-    new_v = [nv[:, :, i:i + 1].contiguous() for i in range(W + K)]
+    new_k = [nk[:, :, i:i + 1].contiguous() for i in range(W + K + D)]
+    new_v = [nv[:, :, i:i + 1].contiguous() for i in range(W + K + D)]
     q = torch.from_numpy(synth.queries(1002, B, U * S * GQ, DH)).to(dev)
     out = torch.empty((B, U * S * GQ, R), dtype=torch.float32, device=dev)
     for c in reps:          # the workspace must cover the longest length of the run
-        c.host_lens += K + W
+        c.host_lens += K + W + D
     ws = [c.workspace(lrkv.MODE_ROPE_RECON, args.n_split) for c in reps]
     for c in reps:
-        c.host_lens -= K + W
+        c.host_lens -= K + W + D
     torch.cuda.synchronize()
 
     if args.copy_probe:
@@ -136,47 +161,61 @@ def main() -> int:
         del src, dst
 
     mode = lrkv.MODE_ROPE_RECON
-    n_ev = 5
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    lens_timed = []
-    log(f"bench: {W} warmup + {K} timed steps, {NR} cache replicas")
-    for i in range(W + K):
+    stream = torch.cuda.current_stream()
+
+    def step(i: int, ev=None) -> int:
+        """One decode step on replica i % NR; ev = events to record around its phases
+        (2: the partials kernel only; 5: every phase)."""
         c, w = reps[i % NR], ws[i % NR]
-        timed = i >= W
-        if i == W:
-            torch.cuda.synchronize()
-            t_start.record()
-        ev = events[i - W] if timed else None
-        if timed:
+        if ev is not None and len(ev) == 5:
             ev[0].record()
-        c.append(new_k[i], new_v[i])
+        c.append(new_k[i], new_v[i], stream=stream)
         L = c.max_len
-        if timed:
+        if ev is not None and len(ev) == 5:
             ev[1].record()
-            lens_timed.append(L)
-        lrkv.decode_prepare(mode, c.desc, q, Bk, None, 0.0, w, L, args.n_split)
-        if timed:
-            ev[2].record()
-        lrkv.decode_partials(mode, c.desc, None, 0.0, w, L, args.n_split)
-        if timed:
-            ev[3].record()
-        lrkv.merge_partials(mode, c.desc, out, w, L, args.n_split)
-        if timed:
+        lrkv.decode_prepare(mode, c.desc, q, Bk, None, 0.0, w, L, args.n_split, stream=stream)
+        if ev is not None:
+            ev[-3 if len(ev) == 5 else 0].record()
+        lrkv.decode_partials(mode, c.desc, None, 0.0, w, L, args.n_split, stream=stream)
+        if ev is not None:
+            ev[-2 if len(ev) == 5 else 1].record()
+        lrkv.merge_partials(mode, c.desc, out, w, L, args.n_split, stream=stream)
+        if ev is not None and len(ev) == 5:
             ev[4].record()
+        return L
+
+    mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    # timed region: K whole steps; the only events inside bracket the partials
+    # kernel (each recorded event costs the GPU a few microseconds)
+    pev = [mk(2) for _ in range(K)]
+    t_start, t_end = mk(2)
+    log(f"bench: {W} warmup + {K} timed steps, {NR} cache replicas")
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    t_start.record()
+    h0 = time.perf_counter()
+    lens_timed = [step(W + k, pev[k]) for k in range(K)]
+    host_us = (time.perf_counter() - h0) / K * 1e6
     t_end.record()
     torch.cuda.synchronize()
-
     total_ms = t_start.elapsed_time(t_end)
-    ph = np.array([[events[k][j].elapsed_time(events[k][j + 1]) for j in range(n_ev - 1)] for k in range(K)])
+    part_each = np.array([a.elapsed_time(b) for a, b in pev])
+    # untimed diagnostic pass: every phase bracketed by events
+    dev_ev = [mk(5) for _ in range(D)]
+    for k in range(D):
+        step(W + K + k, dev_ev[k])
+    torch.cuda.synchronize()
+    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in dev_ev])
+
     lens_timed = np.array(lens_timed, dtype=np.float64)
     bytes_steps = U * B * lens_timed * BYTES_PER_UNIT_TOKEN
     flops_steps = U * B * lens_timed * FLOP_PER_UNIT_TOKEN
     gbs = bytes_steps.sum() / (total_ms * 1e-3) / 1e9
-    part_ms = ph[:, 2].mean()
+    part_ms = part_each.mean()
     achieved = bytes_steps.mean() / (part_ms * 1e-3) / 1e9
     ok = bool(np.isfinite(out.cpu().numpy()).all())
+    traffic = recorded_traffic()
 
     result = {
         "metric": METRIC,
@@ -206,15 +245,19 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
         },
         "detail": {
-            "phase_us": {"append": round(ph[:, 0].mean() * 1e3, 2), "prepare": round(ph[:, 1].mean() * 1e3, 2),
-                         "partials": round(ph[:, 2].mean() * 1e3, 2), "merge": round(ph[:, 3].mean() * 1e3, 2)},
-            "partials_us_p10_p50_p90": [round(float(np.percentile(ph[:, 2], p)) * 1e3, 2) for p in (10, 50, 90)],
+            "phase_us_untimed_pass": {"append": round(ph[:, 0].mean() * 1e3, 2),
+                                      "prepare": round(ph[:, 1].mean() * 1e3, 2),
+                                      "partials": round(ph[:, 2].mean() * 1e3, 2),
+                                      "merge": round(ph[:, 3].mean() * 1e3, 2)},
+            "partials_us_mean_p10_p50_p90": [round(part_ms * 1e3, 2)] +
+                                            [round(float(np.percentile(part_each, p)) * 1e3, 2) for p in (10, 50, 90)],
             "mfma_tflops_partials": round(flops_steps.mean() / (part_ms * 1e-3) / 1e12, 1),
             "mfma_frac_partials": round(flops_steps.mean() / (part_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "bytes_per_step": float(bytes_steps.mean()),
+            "host_submit_us_per_step": round(host_us, 1),
             "output_finite": ok,
         },
     }

@@ -12,7 +12,7 @@
  *    folded into W^o offline, so the output stays in latent space: o = p H^v.
  *    Without RoPE, B^k is absorbed into the query (q' = q (B^k)^T) and the
  *    scores are H^k q'. The Hadamard fold (A R)(R^T B) lets the latents be
- *    stored as int4 (per-token groups of 32, see the Appendix of the digest and
+ *    stored as int4 (per-token groups of 32, see the Supplementary details of the Palu digest and
  *    section 5 of the Shard post for the symmetric [-7, 7] range).
  *  - PuzzleKV: page-based low-rank decomposition for KV-cache compression,
  *    section 3.3. Dense sink / local-window pages plus per-page factors

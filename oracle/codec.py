@@ -5,7 +5,7 @@ quantiser is defined by fixed fp32 / fp16 steps, and the oracle performs exactly
 those steps with numpy float32 / float16 scalars so that codes and scales can be
 compared bit for bit.
 
-Sources: the Palu digest (Appendix, KV-cache compression) uses plain per-token
+Sources: the Palu digest (Supplementary details, KV-cache compression) uses plain per-token
 quantisation and cites group-of-32 fine-grained grouping; the Shard post
 (section 5, step 4) quantises coefficients to symmetric int4 in [-7, 7] with a
 scale per component. Reading used here (the pages fix no rounding rule):

@@ -4,7 +4,7 @@
 // Palu digest, Method details: the cache holds per-token latents h = x A
 // instead of keys and values. PuzzleKV section 3.3, step 5: new key/value pairs
 // go to the newest dense page. The int4 rule (Shard section 5, symmetric
-// [-7, 7]; Palu digest Appendix, per-token groups of 32) is documented in lrkv.h.
+// [-7, 7]; Palu digest, Supplementary details: per-token groups of 32) is documented in lrkv.h.
 #include "common.h"
 
 namespace lrkv {

@@ -3,7 +3,7 @@
 // Palu digest, Method details: keys are cached as latents H^k and rebuilt on
 // chip as K = H^k B^k, RoPE is applied at each token's position, the query
 // attends, and the output stays in latent space, o = p H^v (B^v is folded into
-// W^o offline). Palu digest, Appendix: the sequence is tiled along its length
+// W^o offline). Palu digest, Supplementary details: the sequence is tiled along its length
 // and each tile is reconstructed and scored on chip.
 //
 // Per 32-token tile and query head, the reconstruction GEMM H_tile B (r -> d_h)

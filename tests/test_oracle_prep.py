@@ -55,7 +55,7 @@ def test_no_other_rank_r_factorisation_is_better(tiny):
 
 
 def test_factor_storage_ratio():
-    # (m r + r n)/(m n) for the 4096 x 512 group matrix at rank 256 (Palu digest, Appendix)
+    # (m r + r n)/(m n) for the 4096 x 512 group matrix at rank 256 (Palu digest, Supplementary details)
     assert prep.factor_storage_ratio(4096, 512, 256) == (4096 * 256 + 256 * 512) / (4096 * 512)
     assert prep.factor_storage_ratio(4, 4, 4) == 2.0
 
