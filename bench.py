@@ -70,6 +70,107 @@ def recorded_traffic():
     return float(t.group(1))
 
 
+def _time(torch, fn, iters: int, warmup: int = 3) -> list:
+    """Per-call GPU time (ms) of fn() from HIP events around each call."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def _row(ms: list, nbytes: float, flops: float = 0.0) -> dict:
+    m = float(np.median(ms))
+    out = {"us_median": round(m * 1e3, 2), "us_p10_p90": [round(float(np.percentile(ms, p)) * 1e3, 2) for p in (10, 90)],
+           "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (m * 1e-3) / 1e9, 1),
+           "frac_hbm_peak": round(nbytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if flops:
+        out["tflops"] = round(flops / (m * 1e-3) / 1e12, 1)
+    return out
+
+
+def measure_rows(torch, lrkv, dev, iters: int = 20) -> dict:
+    """The other hot-path rows at their workloads (one decode_attn call each, merge
+    included; factorisation batches). Seeded synthetic inputs generated on the GPU:
+    latents with the decaying spectrum sqrt(s_i) z, low-rank-plus-noise paged K/V."""
+    g = torch.Generator(device=dev)
+    rows = {}
+
+    # absorbed (no RoPE) over fp16 latents: Llama-2-7B layer, 16 sequences of 16K
+    g.manual_seed(3)
+    Bq, Tq = 16, 16384
+    c = lrkv.LatentCache(Bq, U, S, GQ, DH, R, Tq, lrkv.FMT_FP16, 0.0, device=dev)
+    sq = torch.exp(-torch.arange(R, device=dev, dtype=torch.float32) / (2 * TAU))
+    c.hk.copy_((torch.randn(c.hk.shape, generator=g, device=dev) * sq).half())
+    c.hv.copy_((torch.randn(c.hv.shape, generator=g, device=dev) * sq[:, None]).half())
+    c.lens.fill_(Tq)
+    c.host_lens[:] = Tq
+    qa = torch.randn((Bq, U * S * GQ, R), generator=g, device=dev) * 0.35
+    ws = c.workspace(lrkv.MODE_ABSORBED)
+    out = torch.empty((Bq, U * S * GQ, R), dtype=torch.float32, device=dev)
+    ms = _time(torch, lambda: lrkv.decode_attn(lrkv.MODE_ABSORBED, c.desc, qa, None, None, 0.0, out, ws, Tq), iters)
+    rows["absorbed_fp16_B16_T16384"] = _row(ms, Bq * U * Tq * BYTES_PER_UNIT_TOKEN, Bq * U * Tq * 4 * S * R)
+    del c, qa, ws, out
+
+    # RoPE path over Hadamard-rotated int4 latents: Llama-3-8B GQA, rank 64 per KV head
+    g.manual_seed(4)
+    B4, T4, H4, G4, R4 = 4, 65536, 8, 4, 64
+    c = lrkv.LatentCache(B4, H4, 1, G4, DH, R4, T4, lrkv.FMT_INT4_G32, 5e5, device=dev)
+    s4 = torch.exp(-torch.arange(R4, device=dev, dtype=torch.float32) / 64.0)
+    for chunk in range(0, T4, 16384):
+        hk = torch.randn((B4, H4, 16384, R4), generator=g, device=dev) * s4
+        hv = torch.randn((B4, H4, 16384, R4), generator=g, device=dev) * s4
+        c.append(hk, hv)
+    q4 = torch.randn((B4, H4 * G4, DH), generator=g, device=dev)
+    bk4 = (torch.randn((H4, R4, DH), generator=g, device=dev) / 8.0).half()
+    ws = c.workspace(lrkv.MODE_ROPE_RECON)
+    out = torch.empty((B4, H4 * G4, R4), dtype=torch.float32, device=dev)
+    ms = _time(torch, lambda: lrkv.decode_attn(lrkv.MODE_ROPE_RECON, c.desc, q4, bk4, None, 0.0, out, ws, T4), iters)
+    rows["rope_int4_gqa_B4_T65536"] = _row(ms, B4 * H4 * T4 * 72, B4 * H4 * T4 * (2 * R4 * DH + 2 * G4 * DH + 2 * G4 * R4))
+    del c, q4, bk4, ws, out, hk, hv
+
+    # PuzzleKV hybrid: Llama-3.1-8B shape, batch 8, T = 32K, rank-12 pages
+    g.manual_seed(5)
+    B5, H5, G5, T5, P5, RK = 8, 8, 4, 32768, 32, 12
+    pc = lrkv.PagedCache(B5, H5, G5, DH, P5, 1, 4, RK, RK, T5 // P5 + 8, device=dev)
+    def lowrank():
+        z = torch.randn((B5 * H5, T5, RK), generator=g, device=dev)
+        cm = torch.randn((B5 * H5, RK, DH), generator=g, device=dev) / RK ** 0.5
+        x = torch.bmm(z, cm) + 0.05 * torch.randn((B5 * H5, T5, DH), generator=g, device=dev)
+        return x.view(B5, H5, T5, DH).half()
+    k5, v5 = lowrank(), lowrank()
+    pages = torch.from_numpy(lrkv.paged_plan(pc.desc, pc.host_lens, T5)).to(dev)
+    n_fac = int(pages.shape[0])
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    lrkv.factor_page(pc.desc, pages, n_fac, k5, v5, T5, 0)
+    t1.record()
+    lrkv.append_latent(lrkv.MODE_HYBRID_PAGED, pc.desc, k5, v5, T5, 0)
+    pc.host_lens += T5
+    torch.cuda.synchronize()
+    prefill_ms = t0.elapsed_time(t1)
+    q5 = torch.randn((B5, H5 * G5, DH), generator=g, device=dev)
+    ws = pc.workspace()
+    out = torch.empty((B5, H5 * G5, DH), dtype=torch.float32, device=dev)
+    n_dense, n_factored = 5, T5 // P5 - 5
+    by = B5 * H5 * (n_factored * 2 * (P5 * RK + RK * DH) * 2 + n_dense * 2 * P5 * DH * 2)
+    ms = _time(torch, lambda: pc.decode(q5, out=out, workspace=ws), iters)
+    rows["hybrid_paged_B8_T32768"] = _row(ms, by)
+    # one decode step's factorisation batch: one page per (b, head), keys and values
+    step_pages = pages.view(B5, H5, -1, 3)[:, :, -1, :].reshape(-1, 3).contiguous()
+    ms = _time(torch, lambda: lrkv.factor_page(pc.desc, step_pages, step_pages.shape[0], k5, v5, T5, 0), iters)
+    rows["factor_pages_decode_batch"] = {"matrices": 2 * int(step_pages.shape[0]),
+                                         "us_median": round(float(np.median(ms)) * 1e3, 2)}
+    rows["factor_pages_prefill_batch"] = {"matrices": 2 * n_fac, "us": round(prefill_ms * 1e3, 1)}
+    return rows
+
+
 def cpu_baseline(T: int, budget_s: float = 12.0) -> dict:
     """The float64 oracle timed on this host on a bounded sample of the same workload:
     whole units (4 heads each) at full length, until the time budget is used."""
@@ -106,6 +207,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--n-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the timing of the other hot-path rows (absorbed, int4, hybrid, factorisation)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -261,6 +364,11 @@ def main() -> int:
             "output_finite": ok,
         },
     }
+    if not args.no_rows:
+        log("bench: timing the other hot-path rows")
+        del reps, ws
+        torch.cuda.empty_cache()
+        result["detail"]["rows"] = measure_rows(torch, lrkv, dev)
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(T)
