@@ -47,9 +47,10 @@ static void pick_split(int per_split_groups, int host_max_len, int n_split, int 
 
 LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len, int n_split) {
     LatentWorkspace w;
-    // RoPE: ~256 (chunk, unit, sequence) groups, each split over the unit's head
-    // groups; absorbed: ~1024 workgroups of 4 independent waves
-    const int target = mode == LRKV_MODE_ROPE_RECON ? 256 : 1024;
+    // RoPE: ~256 (chunk, unit, sequence) groups at rank 256 (one workgroup per CU),
+    // more for the smaller ranks, whose tiles carry less work each and need more
+    // workgroups in flight; absorbed: ~1024 workgroups of 4 independent waves
+    const int target = mode == LRKV_MODE_ROPE_RECON ? (g.r >= 256 ? 256 : g.r >= 128 ? 512 : 1024) : 1024;
     int cap_split = 1;
     const int max_chunk_tiles = mode == LRKV_MODE_ROPE_RECON ? kMaxRopeTiles : 1 << 30;
     pick_split(g.B * g.U, host_max_len, n_split, target, max_chunk_tiles, &w.n_split, &w.chunk,

@@ -530,7 +530,9 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
     const int g = blockIdx.x;
     if (g >= p.n_groups) return;
     const int u = g % p.U, split = (g / p.U) % p.n_split, b = g / (p.n_split * p.U);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    // the wave index in a scalar register, so that everything derived from it
+    // (load addresses, LDS bases) is scalar arithmetic
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int Hq = p.U * NH;
     const int len = min(p.lens[b], p.cap);
     const int t_begin = split * p.chunk;
@@ -554,35 +556,42 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
     const uint32_t kx = 512u * (l >> 5) + 16u * ((l & 31) ^ (l >> 5));
     const uint32_t vx = 16u * (l ^ vswz(l >> 2));
     // A tile at or past n_tiles gets empty resources: its loads fetch nothing
-    // and write zeros into buffers no longer in use. Each call is 4 loads.
-    auto issue_keys = [&](int tile) {
-        const bool real = tile < n_tiles;
+    // and write zeros into buffers no longer in use. Load n (0..3) of a tile's
+    // keys or values; the loop spreads them over its slices.
+    auto key_load = [&](int tile, int n, bool empty = false) {
+        const bool real = tile < n_tiles && !empty;
         const int r0 = t_begin + 32 * min(tile, n_tiles - 1) + 8 * w;
         const int32x4 kr = make_rsrc(hk + (long)r0 * R, real ? (uint32_t)max(0, len - r0) * (R * 2) : 0u);
-        const half_t* kb = ktile[tile % NBK] + 8 * w * R;
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-            buf_dma16(kr, (kx ^ (16u * (8 * (w & 1) + 2 * n))) + 1024u * n, kb + 2 * n * R);
+        buf_dma16(kr, (kx ^ (16u * (8 * (w & 1) + 2 * n))) + 1024u * n, ktile[tile % NBK] + (8 * w + 2 * n) * R);
     };
-    auto issue_values = [&](int tile) {
+    auto value_load = [&](int tile, int n) {
         const bool real = tile < n_tiles;
         const int t0 = t_begin + 32 * min(tile, n_tiles - 1);
         const int32x4 vr = make_rsrc(hv + (long)(t0 / kTile) * R * kTile + 4 * w * 512, real ? 4096u : 0u);
-        const half_t* vbuf = vtile[tile % NBV] + 4 * w * 512;
+        buf_dma16(vr, vx + 1024u * n, vtile[tile % NBV] + (4 * w + n) * 512);
+    };
+    auto issue_keys = [&](int tile, bool empty = false) {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) buf_dma16(vr, vx + 1024u * n, vbuf + n * 512);
+        for (int n = 0; n < 4; ++n) key_load(tile, n, empty);
+    };
+    auto issue_values = [&](int tile) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) value_load(tile, n);
     };
 
     // Everything the loop starts from is requested at once: the first key and
     // value tiles, Q' and the angle tables (one wait below). Load order: keys 0,
-    // values 0, keys 1, keys 2; then in iteration j (j = 0 in the prologue) keys
-    // j+3 and values j+1. Keys of tile i are waited for at the top of iteration
-    // i: the loads issued after them are then at most 12, 16 and from i = 3 on
-    // 20 (values i-2 and the two following iterations).
+    // values 0, keys 1, (empty), keys 2, (empty); then in iteration j (j = 0 in
+    // the prologue) keys j+3 and values j+1. Keys of tile i are waited for at the
+    // top of iteration i; the loads issued after them are values i-2 and the two
+    // following iterations' loads, and the two empty key loads make that count
+    // the same for i = 1 and 2, so every iteration waits with one count.
     issue_keys(0);
     issue_values(0);
     issue_keys(1);
+    issue_keys(3, true);                       // empty: zeros into key buffer 3
     issue_keys(2);
+    issue_keys(3, true);
     half8 qf[NH][KS];
     {
         // fragment-major Q': one contiguous 1 KB block per (row block, head, K step),
@@ -709,9 +718,7 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
     issue_values(1);
     score_mfma(0);
     for (int i = 1; i < n_tiles; ++i) {
-        if (i >= 3) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-        else if (i == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
         __syncthreads();
         float ps[NH];
 #pragma unroll
@@ -763,9 +770,11 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
             }
             // keys of tile i+3 (their buffer was last read by tile i-1's MFMAs) and
             // values of tile i+1 (buffer last read by tile i-4's product), both
-            // finished by every wave before this tile's barrier
-            if (ks == 1) issue_keys(i + 3);
-            if (ks == 2) issue_values(i + 1);
+            // finished by every wave before this tile's barrier; one load every
+            // other slice, so that no wave stalls long on a full memory queue
+            // while its MFMAs wait behind the load
+            if (ks < 8 && (ks & 1)) key_load(i + 3, ks >> 1);
+            if (ks >= 8 && (ks & 1)) value_load(i + 1, (ks - 8) >> 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
