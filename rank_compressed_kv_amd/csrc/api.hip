@@ -50,7 +50,9 @@ LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len
     // RoPE: ~256 (chunk, unit, sequence) groups at rank 256 (one workgroup per CU),
     // more for the smaller ranks, whose tiles carry less work each and need more
     // workgroups in flight; absorbed: ~1024 workgroups of 4 independent waves
-    const int target = mode == LRKV_MODE_ROPE_RECON ? (g.r >= 256 ? 256 : g.r >= 128 ? 512 : 1024) : 1024;
+    // the grouped-query RoPE kernel: one chunk per wave, two waves per SIMD
+    int target = mode == LRKV_MODE_ROPE_RECON ? (g.r >= 256 ? 256 : g.r >= 128 ? 512 : 1024) : 1024;
+    if (mode == LRKV_MODE_ROPE_RECON && use_gqa_kernel(g)) target = 2048;
     int cap_split = 1;
     const int max_chunk_tiles = mode == LRKV_MODE_ROPE_RECON ? kMaxRopeTiles : 1 << 30;
     pick_split(g.B * g.U, host_max_len, n_split, target, max_chunk_tiles, &w.n_split, &w.chunk,

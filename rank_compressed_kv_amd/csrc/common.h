@@ -88,6 +88,11 @@ int32_t launch_append_paged(const lrkv_paged_cache* c, const half_t* nk, const h
                             int n_new, hipStream_t st);
 // Decode phases: query preparation, per-chunk partial states, split merge.
 constexpr int kPhasePrepare = 1, kPhasePartials = 2, kPhaseMerge = 4, kPhaseAll = 7;
+// What the RoPE preparation writes into the query buffer: Q' row-major, Q' in the
+// frequency-wave kernel's fragment order, or B^k fragments of the grouped-query
+// kernel (which rotates the raw queries itself).
+constexpr int kQpRowMajor = 0, kQpFragments = 1, kQpGqaFragments = 2;
+bool use_gqa_kernel(const LatentGeom& g);
 
 int32_t launch_decode_latent(int mode, int phases, const lrkv_latent_cache* c, const float* q,
                              const half_t* bk, const int32_t* q_pos, float sm_scale, float* out,

@@ -9,17 +9,19 @@ bool rope_fragment_layout(const lrkv_latent_cache* c);
 bool absorbed_shape_supported(int r, int nh);
 void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, const int32_t* lens,
                       half_t* qp, float* qs, float2* angles, int B, int U, int s, int gq, int DH,
-                      int R, int n_split, int chunk, double theta, float scale, bool frag,
-                      hipStream_t st);
+                      int R, int n_split, int chunk, double theta, float scale, int qmode,
+                      bool int4, hipStream_t st);
 int32_t launch_rope_decode(const lrkv_latent_cache* c, const half_t* qp, const float* qs,
                            const float2* angles, float* part, int n_split, int chunk, hipStream_t st);
+int32_t launch_rope_gqa(const lrkv_latent_cache* c, const half_t* qbuf, const float2* angles, float* part,
+                        int n_split, int chunk, hipStream_t st);
 int32_t launch_absorbed_decode(const lrkv_latent_cache* c, const float* q, float* part, int n_split,
                                int chunk, float qscale, hipStream_t st);
 void launch_merge(const float* part, float* out, int BH, int n_split, int D, hipStream_t st);
 
 bool latent_shape_supported(int mode, const LatentGeom& g) {
     const int nh = g.s * g.gq;
-    if (mode == LRKV_MODE_ROPE_RECON) return rope_shape_supported(g.r, g.dh, nh);
+    if (mode == LRKV_MODE_ROPE_RECON) return use_gqa_kernel(g) || rope_shape_supported(g.r, g.dh, nh);
     return absorbed_shape_supported(g.r, nh);
 }
 
@@ -33,12 +35,15 @@ int32_t launch_decode_latent(int mode, int phases, const lrkv_latent_cache* c, c
         half_t* qp = (half_t*)(base + w.qp_off);
         float* qs = (float*)(base + w.qs_off);
         float2* angles = (float2*)(base + w.ang_off);
+        const bool gqa = use_gqa_kernel(g);
+        const int qmode = gqa ? kQpGqaFragments : rope_fragment_layout(c) ? kQpFragments : kQpRowMajor;
         if (phases & kPhasePrepare)
             launch_rope_prep(q, bk, q_pos, c->lens, qp, qs, angles, g.B, g.U, g.s, g.gq, g.dh, g.r,
-                             w.n_split, w.chunk, (double)g.theta, sm_scale * kLog2e,
-                             rope_fragment_layout(c), st);
+                             w.n_split, w.chunk, (double)g.theta, sm_scale * kLog2e, qmode,
+                             g.fmt == LRKV_FMT_INT4_G32, st);
         if (phases & kPhasePartials) {
-            const int32_t rc = launch_rope_decode(c, qp, qs, angles, part, w.n_split, w.chunk, st);
+            const int32_t rc = gqa ? launch_rope_gqa(c, qp, angles, part, w.n_split, w.chunk, st)
+                                   : launch_rope_decode(c, qp, qs, angles, part, w.n_split, w.chunk, st);
             if (rc != LRKV_OK) return rc;
         }
     } else if (phases & kPhasePartials) {

@@ -276,211 +276,6 @@ __global__ __launch_bounds__(256, 2) void rope_decode(const RopeArgs p) {
     }
 }
 
-// ============================================================================ ping-pong kernel
-// fp16 latents, rank 256, head_dim 128, 4 query heads per unit. One workgroup
-// of 8 waves per (chunk, unit): group A (waves 0-3) serves heads 0-1, group B
-// (waves 4-7) heads 2-3, wave w owning feature rows [32 (w%4), +32) of its
-// group's Q' (128 VGPRs of A fragments). The groups run half a tile apart
-// between workgroup barriers:
-//     half-step 2i  : A scores tile i      | B softmax + values of tile i-1
-//     half-step 2i+1: B scores tile i      | A softmax + values of tile i
-// so each SIMD holds one wave issuing score MFMAs and one doing the softmax and
-// the value product. Key and value tiles are loaded once per workgroup with
-// direct global->LDS loads into four buffers, three tiles ahead (every wave
-// issues exactly 6 loads per tile, so the waits count loads):
-//   keys   32 rows of 512 B padded to 528 B (conflict-free B-fragment reads),
-//          written one row per half-wave; rows past t_end re-read the last
-//          valid row and are masked in the softmax;
-//   values the dim-major 32-token block, each 1 KB load covering one 16-dim
-//          M-tile with lane i of the load taking (dim i % 16, tokens 8 (i/16)+0..7),
-//          so the value A fragment of lane l is the 16 bytes at +16 l; tokens
-//          past t_end are zeroed in registers.
-// B fragments are read three K steps ahead of their MFMAs.
-template <int R>
-__global__ __launch_bounds__(512, 1) void rope_decode_pp(const RopeArgs p) {
-    constexpr int DH = 128, NG = 2, KS = R / 16, LDK = R + 8, NBUF = 4, AHEAD = 3;
-    constexpr int VMW = (R / 16) / 4;          // value M-tiles per wave
-    constexpr int LOADS = 6;                   // global->LDS loads per wave per tile
-    static_assert(R == 256, "ping-pong kernel covers rank 256");
-    __shared__ __attribute__((aligned(16))) half_t ktile[NBUF][32 * LDK];
-    __shared__ __attribute__((aligned(16))) half_t vtile[NBUF][R * 32];
-    __shared__ float spart[2][4][32][NG];
-    __shared__ __attribute__((aligned(16))) half_t pbuf[8][NG][32];
-    __shared__ float2 stab[4][2][8];           // per-tile rotation of (M-tile, half-wave)
-
-    const int g = blockIdx.x;
-    if (g >= p.n_groups) return;
-    const int split = g % p.n_split, u = (g / p.n_split) % p.U, b = g / (p.n_split * p.U);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int grp = w >> 2, mt = w & 3;
-    const int Hq = p.U * 4, j0 = u * 4 + grp * NG;
-    const int len = min(p.lens[b], p.cap);
-    const int t_begin = split * p.chunk;
-    const int t_end = min(len, t_begin + p.chunk);
-    const long bu = (long)b * p.U + u;
-    const long hstride = (long)p.n_split * (R + 2);
-    float* part = p.part + ((long)(b * Hq + j0) * p.n_split + split) * (R + 2);
-    if (t_begin >= t_end) {
-        write_empty(p.part + ((long)(b * Hq + u * 4) * p.n_split + split) * (R + 2), hstride, 4, R, tid, 512);
-        return;
-    }
-    const int n_tiles = (t_end - t_begin + 31) / 32;
-    const half_t* hk = (const half_t*)p.hk + bu * p.cap * R;
-    const half_t* hv = (const half_t*)p.hv + bu * p.cap * R;      // [cap/32][R][32]
-
-    auto issue_tile = [&](int tile) {
-        const int t0 = t_begin + 32 * tile, bsel = tile % NBUF;
-        // keys: rows 4w .. 4w+3, one row per half-wave (LDS address from uniform values)
-#pragma unroll 1
-        for (int n = 0; n < 4; ++n) {
-            const int hsel = n & 1, row = 4 * w + n;
-            if ((l >> 5) == hsel)
-                dma16_async(hk + (long)min(t0 + row, t_end - 1) * R + (l & 31) * 8,
-                            ktile[bsel] + row * LDK - hsel * 256);
-        }
-        // values: 1 KB M-tiles 2w, 2w+1 of the block
-        const half_t* vb = hv + (long)(t0 / kTile) * R * kTile;
-#pragma unroll 1
-        for (int n = 2 * w; n < 2 * w + 2; ++n)
-            dma16_async(vb + (16 * n + (l & 15)) * kTile + 8 * (l >> 4), vtile[bsel] + n * 512);
-    };
-
-    float cs[8], sn[8];
-    {
-        float stc[8], sts[8];
-        init_angles(p, b, split, bu, mt, l, DH, cs, sn, stc, sts);
-        if ((l & 31) == 0) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) stab[mt][l >> 5][k] = make_float2(stc[k], sts[k]);
-        }
-    }
-    half8 afrag[NG][KS];
-#pragma unroll
-    for (int h = 0; h < NG; ++h) {
-        const half_t* src = p.qp + (((long)b * Hq + j0 + h) * DH + 32 * mt + (l & 31)) * R + 8 * (l >> 5);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) afrag[h][kk] = *reinterpret_cast<const half8*>(src + 16 * kk);
-    }
-    float m_run[NG], l_run[NG];
-    floatx4 accv[VMW];
-#pragma unroll
-    for (int h = 0; h < NG; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.0f; }
-#pragma unroll
-    for (int v = 0; v < VMW; ++v) accv[v] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // query fragments and angle tables: a real s_waitcnt vmcnt(0), which the
-    // compiler's wait tracking sees, so it adds no waits for them inside the loop
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    for (int t = 0; t < AHEAD && t < n_tiles; ++t) issue_tile(t);
-    // tile 0 complete: the loads of min(n_tiles, AHEAD) - 1 later tiles may remain
-    if (n_tiles >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if (n_tiles == 2) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else wait_vmem();
-    __syncthreads();
-
-    for (int hs = 0; hs <= 2 * n_tiles; ++hs) {
-        if (hs & 1) {
-            // tile i+1 must have landed (i = (hs-1)/2); then fetch tile i+3
-            const int i = (hs - 1) / 2;
-            if (i + 2 < n_tiles) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-            else wait_vmem();
-            if (i + 3 < n_tiles) issue_tile(i + 3);
-        }
-        const bool score = grp == 0 ? ((hs & 1) == 0 && hs < 2 * n_tiles) : (hs & 1);
-        const bool soft = grp == 0 ? (hs & 1) : ((hs & 1) == 0 && hs >= 2);
-        if (score) {
-            const int tile = grp == 0 ? hs / 2 : (hs - 1) / 2;
-            const half_t* brow = ktile[tile % NBUF] + (l & 31) * LDK + 8 * (l >> 5);
-            floatx16 acc[NG];
-#pragma unroll
-            for (int h = 0; h < NG; ++h) acc[h] = floatx16{};
-            half8 bq[AHEAD];
-#pragma unroll
-            for (int a = 0; a < AHEAD; ++a) bq[a] = *reinterpret_cast<const half8*>(brow + 16 * a);
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const half8 cur = bq[kk % AHEAD];
-                if (kk + AHEAD < KS) bq[kk % AHEAD] = *reinterpret_cast<const half8*>(brow + 16 * (kk + AHEAD));
-#pragma unroll
-                for (int h = 0; h < NG; ++h) acc[h] = mfma32(afrag[h][kk], cur, acc[h]);
-            }
-            // keep AHEAD fragment reads in flight: reads, then (2 MFMA, 1 read) ..., then MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-            for (int kk = 0; kk < KS - AHEAD; ++kk) {
-                __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NG * AHEAD, 0);
-#pragma unroll
-            for (int h = 0; h < NG; ++h) {
-                const float ps = rope_combine(acc[h], cs, sn);
-                if (l < 32) spart[grp][mt][l][h] = ps;
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float2 st = stab[mt][l >> 5][k];
-                const float c2 = fmaf(cs[k], st.x, -sn[k] * st.y);
-                const float s2 = fmaf(sn[k], st.x, cs[k] * st.y);
-                cs[k] = c2;
-                sn[k] = s2;
-            }
-        } else if (soft) {
-            const int tile = grp == 0 ? (hs - 1) / 2 : hs / 2 - 1;
-            const int t0 = t_begin + 32 * tile;
-            const int tok = l & 31;
-            const bool valid = t0 + tok < t_end;
-            float alpha[NG];
-#pragma unroll
-            for (int h = 0; h < NG; ++h) {
-                float sc = spart[grp][0][tok][h] + spart[grp][1][tok][h] + spart[grp][2][tok][h] +
-                           spart[grp][3][tok][h];
-                sc = valid ? sc : -INFINITY;
-                const float mn = fmaxf(m_run[h], half_max32(sc));
-                alpha[h] = exp2f(m_run[h] - mn);
-                const float pv = valid ? exp2f(sc - mn) : 0.0f;
-                l_run[h] = fmaf(l_run[h], alpha[h], half_sum32(pv));
-                m_run[h] = mn;
-                if (l < 32) pbuf[w][h][tok] = (half_t)pv;
-            }
-            __builtin_amdgcn_wave_barrier();
-            const int hn = l & 15;
-            const float a_hn = hn == 0 ? alpha[0] : (hn == 1 ? alpha[1] : 1.0f);
-            const half8 pf = hn < NG ? *reinterpret_cast<const half8*>(&pbuf[w][hn < NG ? hn : 0][8 * (l >> 4)])
-                                     : half8{};
-            const half_t* vt = vtile[tile % NBUF];
-            const bool tail = t0 + 32 > t_end;
-#pragma unroll
-            for (int v = 0; v < VMW; ++v) {
-                const int mv = mt * VMW + v;
-                half8 a = *reinterpret_cast<const half8*>(vt + mv * 512 + 8 * l);
-                if (tail) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (t0 + 8 * (l >> 4) + e >= t_end) a[e] = (half_t)0.0f;
-                }
-                accv[v] *= a_hn;
-                accv[v] = mfma16(a, pf, accv[v]);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (mt == 0 && l < NG) {
-        part[l * hstride + 0] = m_run[l];
-        part[l * hstride + 1] = l_run[l];
-    }
-    const int hn = l & 15;
-    if (hn < NG) {
-#pragma unroll
-        for (int v = 0; v < VMW; ++v) {
-            const int mv = mt * VMW + v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) part[hn * hstride + 2 + 16 * mv + 4 * (l >> 4) + e] = accv[v][e];
-        }
-    }
-}
-
 // ============================================================================ frequency-wave kernel
 // fp16 latents, rank 256, head_dim 128, 4 query heads per unit. One workgroup
 // of 4 waves per (chunk, unit). Wave w owns feature rows [32 w, 32 w + 32) of

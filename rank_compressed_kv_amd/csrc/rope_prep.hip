@@ -115,14 +115,49 @@ __global__ __launch_bounds__(256) void rope_angles(float2* __restrict__ tab,
     tab[e] = make_float2((float)cd, (float)sd);
 }
 
+// B^k of one-KV-head units (d_h = 128) in the 16x16x32 MFMA A-fragment order of
+// the grouped-query kernel: bf[u][mt][ks][lane][e] = B^k[u][rank][dim] with
+// dim = 16 mt + lane % 16 and rank = R/4 (lane / 16) + 8 ks + perm(e). For int4
+// latents perm = (0, 4, 1, 5, 2, 6, 3, 7), the order in which that kernel unpacks
+// a word of codes; identity for fp16.
+__global__ __launch_bounds__(256) void gqa_bfrag(const half_t* __restrict__ bk, half_t* __restrict__ bf,
+                                                 int U, int R, int int4) {
+    const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int KS = R / 32;
+    if (e >= (long)U * 128 * R) return;
+    const int el = (int)(e & 7), lane = (int)((e >> 3) & 63);
+    const long rest = e >> 9;
+    const int ks = (int)(rest % KS), mt = (int)((rest / KS) % 8), u = (int)(rest / (KS * 8));
+    const int pe = int4 ? ((el & 1) ? 4 + (el >> 1) : (el >> 1)) : el;
+    const int rank = (R / 4) * (lane >> 4) + 8 * ks + pe, dim = 16 * mt + (lane & 15);
+    bf[e] = bk[((long)u * R + rank) * 128 + dim];
+}
+
+// Queries of the grouped-query kernel: q x sm_scale x log2(e), fp32, same layout.
+__global__ __launch_bounds__(256) void gqa_qscale(const float* __restrict__ q, float* __restrict__ qo, long n,
+                                                  float scale) {
+    const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < n) qo[e] = q[e] * scale;
+}
+
 }  // namespace
 
 void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, const int32_t* lens,
                       half_t* qp, float* qs, float2* angles, int B, int U, int s, int gq, int DH,
-                      int R, int n_split, int chunk, double theta, float scale, bool frag,
-                      hipStream_t st) {
-    hipLaunchKernelGGL(rope_qprep, dim3(B * U, DH / 8), dim3(256), 0, st, q, bk, qp, qs, U, s, gq, DH,
-                       R, scale, frag);
+                      int R, int n_split, int chunk, double theta, float scale, int qmode,
+                      bool int4, hipStream_t st) {
+    if (qmode == kQpGqaFragments) {
+        // B^k fragments, then the scaled queries right after them
+        const long n = (long)U * 128 * R;
+        hipLaunchKernelGGL(gqa_bfrag, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, bk, qp, U, R,
+                           int4 ? 1 : 0);
+        const long nq = (long)B * U * s * gq * DH;
+        hipLaunchKernelGGL(gqa_qscale, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, q,
+                           reinterpret_cast<float*>(qp + n), nq, scale);
+    } else {
+        hipLaunchKernelGGL(rope_qprep, dim3(B * U, DH / 8), dim3(256), 0, st, q, bk, qp, qs, U, s, gq,
+                           DH, R, scale, qmode == kQpFragments);
+    }
     const int n = (33 + B * n_split) * (DH / 2);
     hipLaunchKernelGGL(rope_angles, dim3((n + 255) / 256), dim3(256), 0, st, angles, q_pos, lens, B,
                        n_split, chunk, DH / 2, theta);

@@ -160,6 +160,36 @@ def test_rope_int4_parity(name, T, cap, ragged):
     assert err.max() <= TOL, err.max()
 
 
+@pytest.mark.parametrize("fmt_name,T,cap,ragged,n_split", [
+    ("int4", 31, 32, (), 0),                 # one partial tile
+    ("int4", 4097, 4128, (0, 4000), 0),      # ragged: 97 tokens in sequence 1
+    ("fp16", 777, 800, (0, 1), 3),
+    ("int4", 2000, 2048, (5, 0), 1),         # one chunk of 63 tiles per (sequence, unit)
+    ("fp16", 32, 32, (), 0),                 # exactly one tile
+])
+def test_rope_gqa_edges(fmt_name, T, cap, ragged, n_split):
+    """Grouped-query units (one KV head, 4 query heads, rank 64): tile tails,
+    ragged lengths and chunkings of the reconstruct-then-rotate kernel."""
+    R = _R()
+    fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
+    say(f"rope gqa edges: {fmt_name} T={T} ragged={ragged} n_split={n_split}")
+    c = _make("llama3_gqa", T, cap, fmt, seed=26, ragged=ragged, mixed=fmt_name == "int4")
+    err = rel_l2(_gpu_rope(c, n_split=n_split), _oracle_rope(c))
+    say(f"  max rel-L2 {err.max():.3g}")
+    assert err.max() <= TOL, err.max()
+
+
+def test_rope_gqa_split_independence():
+    R = _R()
+    say("rope gqa split independence: llama3_gqa int4 T=3000, n_split 1/2/5/auto")
+    c = _make("llama3_gqa", 3000, 3008, R.FMT_INT4_G32, seed=27, mixed=True)
+    ref = _oracle_rope(c)
+    outs = [_gpu_rope(c, n_split=n) for n in (1, 2, 5, 0)]
+    for o in outs:
+        assert rel_l2(o, ref).max() <= TOL
+        assert rel_l2(o, outs[0]).max() <= 2 * 2.0 ** -11
+
+
 def test_rope_split_independence():
     R = _R()
     say("rope split independence: llama2_glrd T=1500, n_split 1/3/7/auto")
@@ -242,3 +272,33 @@ def test_rope_full_size_sampled():
                    Bk=c["Bk"][u:u + 1, :, w * 128:(w + 1) * 128], s=1, gq=1)
         ref = _oracle_rope(sub)
         assert rel_l2(got[:, j], ref[:, 0]).max() <= TOL
+
+
+def test_rope_gqa_full_size_sampled():
+    """Llama-3-8B GQA shape, int4 latents, batch 4 at T = 64K in the bench's launch
+    configuration; one query head of each KV head of sequences 0 and 3 checked
+    against the oracle one by one."""
+    R = _R()
+    T, B = 65536, 4
+    say(f"rope gqa full size: int4 B={B} T={T} (sampled heads)")
+    U, s, gq, dh, r, th = 8, 1, 4, 128, 64, 5e5
+    lay = synth.latent_layer(3, B, U, T, r, dh, 32.0)
+    hk, Bk = synth.hadamard_mixed(lay["hk"], lay["Bk"])
+    hv, _ = synth.hadamard_mixed(lay["hv"], lay["Bv"])
+    q = synth.queries(1003, B, U * gq, dh, 1.0)
+    cache = R.LatentCache(B, U, s, gq, dh, r, T, R.FMT_INT4_G32, th)
+    cache.append(to_dev(hk), to_dev(hv))
+    got = cache.decode(R.MODE_ROPE_RECON, to_dev(q), to_dev(Bk))
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.isfinite(got).all()
+    lens = np.full(B, T, np.int64)
+    for u in range(U):
+        j = u * gq + (u % gq)
+        for b in (0, 3):
+            ref = oattn.palu_decode(oattn.stored_int4(hk[b:b + 1, u:u + 1]),
+                                    oattn.stored_int4(hv[b:b + 1, u:u + 1]),
+                                    Bk[u:u + 1].astype(np.float64), q[b:b + 1, j:j + 1], lens[:1],
+                                    1, 1, dh, th)
+            err = rel_l2(got[b:b + 1, j], ref[:, 0]).max()
+            assert err <= TOL, (u, b, err)
