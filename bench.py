@@ -289,8 +289,10 @@ def main() -> int:
 
     mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     # timed region: K whole steps; the only events inside bracket the partials
-    # kernel (each recorded event costs the GPU a few microseconds)
-    pev = [mk(2) for _ in range(K)]
+    # kernel of every EVERY-th step (each recorded event costs the GPU a few
+    # microseconds, so sampling keeps that cost out of most steps)
+    EVERY = 4
+    pev = [mk(2) if k % EVERY == 0 else None for k in range(K)]
     t_start, t_end = mk(2)
     log(f"bench: {W} warmup + {K} timed steps, {NR} cache replicas")
     for i in range(W):
@@ -303,7 +305,7 @@ def main() -> int:
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    part_each = np.array([a.elapsed_time(b) for a, b in pev])
+    part_each = np.array([e[0].elapsed_time(e[1]) for e in pev if e is not None])
     # untimed diagnostic pass: every phase bracketed by events
     dev_ev = [mk(5) for _ in range(D)]
     for k in range(D):
