@@ -58,13 +58,20 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
     {
         float qv[KS][8];
         float mx = 0.0f;
+        // unconditional 16-byte loads (padding heads read head NH - 1, then zero)
+        const float* qrow = p.q + ((long)b * Hq + j0 + (hn < NH ? hn : NH - 1)) * R + 8 * g;
+        const float qs = hn < NH ? p.qscale : 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
+        for (int kk = 0; kk < KS; ++kk) {
+            const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * kk);
+            const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * kk + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qv[kk][e] = hn < NH ? p.q[((long)b * Hq + j0 + hn) * R + 32 * kk + 8 * g + e] * p.qscale : 0.0f;
+                qv[kk][e] = xs[e] * qs;
                 mx = fmaxf(mx, fabsf(qv[kk][e]));
             }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
         const int ex = (mx > 0.0f && isfinite(mx)) ? 14 - ilogbf(mx) : 0;
@@ -83,27 +90,59 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
     const int n_tiles = (t_end - t_begin + 31) / 32;
     for (int it = w; it < n_tiles; it += 4) {
         const int t0 = t_begin + 32 * it;
+        const bool tail = t0 + 32 > t_end;
+        const long blk_base = bu * (p.cap / kTile) + t0 / kTile;
+        // every load of the tile is issued before the first MFMA: key rows
+        // t0 + 16 mt + hn (clamped to the last valid token; their scores are
+        // masked), value dims 16 v + hn at tokens {4g..4g+3, 16+4g..16+4g+3}
+        half8 ka[2][KS], va[VM];
+        uint32_t kcode[2][KS], vlo[VM], vhi[VM];
+        half_t ksc[2][KS];
+        half4 vslo[VM], vshi[VM];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const long row = bu * p.cap + min(t0 + 16 * mt + hn, t_end - 1);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                if constexpr (!INT4) {
+                    ka[mt][kk] = *reinterpret_cast<const half8*>((const half_t*)p.hk + row * R + 32 * kk + 8 * g);
+                } else {
+                    kcode[mt][kk] = *reinterpret_cast<const uint32_t*>((const uint8_t*)p.hk + row * (R / 2) + 16 * kk + 4 * g);
+                    ksc[mt][kk] = p.sk[row * (R / 32) + kk];
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VM; ++v) {
+            const int dim = 16 * v + hn;
+            if constexpr (!INT4) {
+                const half_t* src = (const half_t*)p.hv + (blk_base * R + dim) * kTile;
+                const half4 lo = *reinterpret_cast<const half4*>(src + 4 * g);
+                const half4 hi = *reinterpret_cast<const half4*>(src + 16 + 4 * g);
+                va[v] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                const uint8_t* src = (const uint8_t*)p.hv + (blk_base * R + dim) * (kTile / 2);
+                vlo[v] = *reinterpret_cast<const uint16_t*>(src + 2 * g);
+                vhi[v] = *reinterpret_cast<const uint16_t*>(src + 8 + 2 * g);
+                const half_t* ss = p.sv + (blk_base * (R / 32) + dim / 32) * kTile;
+                vslo[v] = *reinterpret_cast<const half4*>(ss + 4 * g);
+                vshi[v] = *reinterpret_cast<const half4*>(ss + 16 + 4 * g);
+            }
+        }
         // scores: two 16-token M-tiles; lane holds tokens 16mt + 4g + e for head hn
         floatx4 sc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             sc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const int row = t0 + 16 * mt + hn;
-            const bool ok = row < t_end;
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 half8 a;
                 if constexpr (!INT4) {
-                    a = ok ? *reinterpret_cast<const half8*>((const half_t*)p.hk + (bu * p.cap + row) * R + 32 * kk + 8 * g)
-                           : half8{};
+                    a = ka[mt][kk];
                 } else {
-                    a = half8{};
-                    if (ok) {
-                        const uint32_t code = *reinterpret_cast<const uint32_t*>((const uint8_t*)p.hk + (bu * p.cap + row) * (R / 2) + 16 * kk + 4 * g);
-                        const float s = (float)p.sk[(bu * p.cap + row) * (R / 32) + kk];
+                    const float s = (float)ksc[mt][kk];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) a[e] = (half_t)((float)nibble(code, e) * s);
-                    }
+                    for (int e = 0; e < 8; ++e) a[e] = (half_t)((float)nibble(kcode[mt][kk], e) * s);
                 }
                 sc[mt] = mfma16(a, qf[kk], sc[mt]);
             }
@@ -137,36 +176,30 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
         m_run = mn;
         if (hn >= NH) pf = half8{};
         // values: A = V^T [16 dims][tokens {4g..4g+3, 16+4g..16+4g+3}]
-        const long blk_base = bu * (p.cap / kTile) + t0 / kTile;
+        if constexpr (INT4) {
 #pragma unroll
-        for (int v = 0; v < VM; ++v) {
-            const int dim = 16 * v + hn;
-            half8 a;
-            if constexpr (!INT4) {
-                const half_t* src = (const half_t*)p.hv + (blk_base * R + dim) * kTile;
-                const half4 lo = *reinterpret_cast<const half4*>(src + 4 * g);
-                const half4 hi = *reinterpret_cast<const half4*>(src + 16 + 4 * g);
-                a = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-                const uint8_t* src = (const uint8_t*)p.hv + (blk_base * R + dim) * (kTile / 2);
-                const uint32_t clo = *reinterpret_cast<const uint16_t*>(src + 2 * g);
-                const uint32_t chi = *reinterpret_cast<const uint16_t*>(src + 8 + 2 * g);
-                const half_t* ss = p.sv + (blk_base * (R / 32) + dim / 32) * kTile;
-                const half4 slo = *reinterpret_cast<const half4*>(ss + 4 * g);
-                const half4 shi = *reinterpret_cast<const half4*>(ss + 16 + 4 * g);
+            for (int v = 0; v < VM; ++v)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    a[e] = (half_t)((float)nibble(clo, e) * (float)slo[e]);
-                    a[4 + e] = (half_t)((float)nibble(chi, e) * (float)shi[e]);
+                    va[v][e] = (half_t)((float)nibble(vlo[v], e) * (float)vslo[v][e]);
+                    va[v][4 + e] = (half_t)((float)nibble(vhi[v], e) * (float)vshi[v][e]);
                 }
-            }
+        }
+        if (tail) {
+            // tokens past t_end: zero (their p is zero; the memory may hold anything)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int t = t0 + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-                if (t >= t_end) a[e] = (half_t)0.0f;
+                if (t >= t_end) {
+#pragma unroll
+                    for (int v = 0; v < VM; ++v) va[v][e] = (half_t)0.0f;
+                }
             }
+        }
+#pragma unroll
+        for (int v = 0; v < VM; ++v) {
             acc[v] *= alpha;
-            acc[v] = mfma16(a, pf, acc[v]);
+            acc[v] = mfma16(va[v], pf, acc[v]);
         }
     }
 
