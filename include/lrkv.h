@@ -112,10 +112,20 @@ typedef struct lrkv_latent_cache {
  * page p < sink_pages uses slot p; any other dense page uses slot
  * sink_pages + (p - sink_pages) % window_pages.
  *
- *   dense_k, dense_v [batch][kv_heads][sink_pages+window_pages][P][head_dim] half
- *   lk, lv           [batch][kv_heads][max_pages][P][rank]                  half
- *   rk, rv           [batch][kv_heads][max_pages][rank][head_dim]           half
- *   page_table       [batch][kv_heads][max_pages]                           int32
+ *   dense_k     [batch][kv_heads][sink_pages+window_pages][P][head_dim]  half
+ *   dense_v     [batch][kv_heads][sink_pages+window_pages][head_dim][P]  half
+ *   lk          [batch][kv_heads][max_pages][P][rank_k]                  half  L_K
+ *   rk          [batch][kv_heads][max_pages][rank_k][head_dim]           half  R_K
+ *   lv          [batch][kv_heads][max_pages][rank_v][P]                  half  L_V^T
+ *   rv          [batch][kv_heads][max_pages][head_dim][rank_v]           half  R_V^T
+ *   page_table  [batch][kv_heads][max_pages]                             int32
+ *
+ * A factored page holds X_hat = L R (PuzzleKV Eq. 2: L = the page's top left
+ * singular vectors, R = Sigma W^T). Key-side arrays are stored as L and R, the
+ * value side transposed (dimension-major), as are the dense values: each decode
+ * product then reads a contiguous run of its contraction index. Supported:
+ * head_dim 128, P 32, q_per_kv <= 16, ranks multiples of 4 up to 32,
+ * max_pages <= 65536 (LRKV_ERR_UNSUPPORTED otherwise).
  */
 #define LRKV_PAGE_EMPTY ((int32_t)0x80000000)
 

@@ -186,12 +186,13 @@ class PagedCache:
         dev = torch.device(device)
         nd = sink_pages + window_pages
         f16 = torch.float16
+        # keys row-major; values (dense and factored) dimension-major
         self.dense_k = torch.zeros((batch, kv_heads, nd, page_size, head_dim), dtype=f16, device=dev)
-        self.dense_v = torch.zeros_like(self.dense_k)
+        self.dense_v = torch.zeros((batch, kv_heads, nd, head_dim, page_size), dtype=f16, device=dev)
         self.lk = torch.zeros((batch, kv_heads, max_pages, page_size, rank_k), dtype=f16, device=dev)
         self.rk = torch.zeros((batch, kv_heads, max_pages, rank_k, head_dim), dtype=f16, device=dev)
-        self.lv = torch.zeros((batch, kv_heads, max_pages, page_size, rank_v), dtype=f16, device=dev)
-        self.rv = torch.zeros((batch, kv_heads, max_pages, rank_v, head_dim), dtype=f16, device=dev)
+        self.lv = torch.zeros((batch, kv_heads, max_pages, rank_v, page_size), dtype=f16, device=dev)
+        self.rv = torch.zeros((batch, kv_heads, max_pages, head_dim, rank_v), dtype=f16, device=dev)
         self.page_table = torch.full((batch, kv_heads, max_pages), PAGE_EMPTY, dtype=torch.int32, device=dev)
         self.lens = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.host_lens = np.zeros(batch, dtype=np.int64)

@@ -76,9 +76,12 @@ LatentWorkspace latent_workspace(int mode, const LatentGeom& g, int host_max_len
 
 PagedWorkspace paged_workspace(const lrkv_paged_cache* c, int host_max_len, int n_split) {
     PagedWorkspace w;
-    const int npg = (host_max_len + c->page_size - 1) / c->page_size;
+    int npg = (host_max_len + c->page_size - 1) / c->page_size;
+    if (npg > c->max_pages) npg = c->max_pages;
     const int groups = c->batch * c->kv_heads;
+    // about one wave per SIMD slot (two per SIMD); a wave takes at most 64 pages
     if (n_split <= 0) n_split = (2048 + groups - 1) / groups;
+    if (n_split < (npg + 63) / 64) n_split = (npg + 63) / 64;
     if (n_split > kMaxSplit) n_split = kMaxSplit;
     if (n_split > npg) n_split = npg;
     if (n_split < 1) n_split = 1;
@@ -119,9 +122,12 @@ static int32_t check_paged(const lrkv_paged_cache* c) {
     if (!c->dense_k || !c->dense_v || !c->lk || !c->rk || !c->lv || !c->rv || !c->page_table ||
         !c->lens)
         return LRKV_ERR_INVALID_ARG;
-    if (c->head_dim != 128 || c->page_size != 32 || c->q_per_kv > 4 || c->rank_k > 32 ||
-        c->rank_v > 32)
+    if (c->head_dim != 128 || c->page_size != 32 || c->q_per_kv > 16 || c->rank_k > 32 ||
+        c->rank_v > 32 || (c->rank_k % 4) || (c->rank_v % 4))
         return LRKV_ERR_UNSUPPORTED;
+    // one (sequence, head)'s factor arrays are addressed with 32-bit byte offsets
+    if ((size_t)c->max_pages * 32 * 128 * 2 >= ((size_t)1 << 31)) return LRKV_ERR_UNSUPPORTED;
+    if (c->max_pages > 64 * kMaxSplit) return LRKV_ERR_UNSUPPORTED;
     if (!aligned16(c->dense_k) || !aligned16(c->dense_v) || !aligned16(c->rk) || !aligned16(c->rv))
         return LRKV_ERR_INVALID_ARG;
     return LRKV_OK;

@@ -179,7 +179,8 @@ __global__ void append_int4_v(const float* __restrict__ nv, uint8_t* __restrict_
 }
 
 // Hybrid cache: one thread per (b, h, i, 8 dims) copying K and V into the dense
-// slot of the token's page, unless that page is already factored.
+// slot of the token's page (values transposed), unless that page is already
+// factored.
 __global__ void append_paged(const half_t* __restrict__ nk, const half_t* __restrict__ nv,
                              half_t* __restrict__ dk, half_t* __restrict__ dv,
                              int32_t* __restrict__ table, const int32_t* __restrict__ lens, int B,
@@ -201,9 +202,12 @@ __global__ void append_paged(const half_t* __restrict__ nk, const half_t* __rest
     if (*entry >= 0) return;                 // factored already (prefill)
     const int slot = p < sink ? p : sink + (p - sink) % window;
     const long src = (bh * n_new + i) * d + c8 * 8;
-    const long dst = ((bh * (sink + window) + slot) * P + pos % P) * d + c8 * 8;
-    *reinterpret_cast<half8*>(dk + dst) = *reinterpret_cast<const half8*>(nk + src);
-    *reinterpret_cast<half8*>(dv + dst) = *reinterpret_cast<const half8*>(nv + src);
+    const long page = bh * (sink + window) + slot;
+    // keys row-major [P][d], values dimension-major [d][P]
+    *reinterpret_cast<half8*>(dk + (page * P + pos % P) * d + c8 * 8) = *reinterpret_cast<const half8*>(nk + src);
+    const half8 v = *reinterpret_cast<const half8*>(nv + src);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dv[(page * d + c8 * 8 + e) * P + pos % P] = v[e];
     if (pos % P == 0 && c8 == 0) *entry = -1 - slot;
 }
 

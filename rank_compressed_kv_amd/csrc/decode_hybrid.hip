@@ -6,11 +6,25 @@
 // (a L_V) R_V (the value side follows by associativity; the page's text stops
 // after the key-side formula). All partial results are merged by online softmax.
 //
-// Work split: one workgroup (4 waves) per (page range, KV head, sequence); the
-// waves take pages round-robin and keep private (m, l, o) states that are merged
-// in LDS at the end; chunks are merged by merge_splits. Lane l serves query head
-// l/16 of the KV head and dims [8 (l%16), 8 (l%16) + 8); sums over a head's 16
-// lanes use DPP row operations.
+// One wave streams the pages of one (page range, KV head, sequence); the
+// range's chunk states are merged by merge_splits. Every product of a page is a
+// 16x16 MFMA whose output fragment is already the next product's operand
+// (lane l: column c = l % 16 = query head, lane group g = l / 16):
+//   U^T [rank][head]  = R_K Q^T          16x16x32, A = R_K rows (rank c), K = 128 dims
+//   S   [tok][head]   = L_K U^T          16x16x16, A = L_K rows (token c), K = ranks
+//   online softmax: lane (c, g) holds head c at tokens 16 tb + 4 g + i
+//   W^T [rank][head]  = L_V^T P^T        16x16x16, A = L_V^T rows (rank c), K = tokens
+//   O^T [dim][head]  += R_V^T W^T        16x16x16, A = R_V^T rows (dim c), K = ranks
+// so the value-side factors are stored dimension-major (L_V^T [r][P],
+// R_V^T [d][r]), as are dense values (V^T [d][P]): every operand is a
+// contiguous run of the contraction index. Heads c >= G are zero columns.
+// Query and u = q R_K^T enter the MFMA as fp16 hi + lo pairs (u's magnitude
+// grows with the factor scale; one fp16 rounding of it would cost ~1e-3 of the
+// output), p and w once rounded to fp16.
+//
+// Factored pages stream through three register buffers (two pages in flight
+// while one is computed); dense pages (sink and window, a handful per
+// sequence) are handled after them without pipelining.
 #include "common.h"
 
 #include <math.h>
@@ -18,174 +32,317 @@
 namespace lrkv {
 namespace {
 
-// DPP controls (gfx9): quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float row_sum16(float v) {
-    v += dpp<0xB1>(v);
-    v += dpp<0x4E>(v);
-    v += dpp<0x141>(v);
-    v += dpp<0x140>(v);
-    return v;
-}
-__device__ __forceinline__ float row_max16(float v) {
-    v = fmaxf(v, dpp<0xB1>(v));
-    v = fmaxf(v, dpp<0x4E>(v));
-    v = fmaxf(v, dpp<0x141>(v));
-    v = fmaxf(v, dpp<0x140>(v));
-    return v;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 mfma16k16(half4 a, half4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void load8(const half_t* p, float* o) {
-    const half8 h = *reinterpret_cast<const half8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (float)h[e];
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rs(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// Offsets at or past the resource size read as zero: `kOff` marks a masked lane.
+constexpr uint32_t kOff = 0x80000000u;
+__device__ __forceinline__ half8 ld8(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ half4 ld4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// max / sum over the four lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float xg_max(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    v = fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float xg_sum(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    v = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+__device__ __forceinline__ half4 to_half4(floatx4 v) {
+    return half4{(half_t)v[0], (half_t)v[1], (half_t)v[2], (half_t)v[3]};
+}
+// v = hi + lo with hi = fp16(v), lo = fp16(v - hi)
+__device__ __forceinline__ void split4(floatx4 v, half4& hi, half4& lo) {
+    hi = to_half4(v);
+    lo = half4{(half_t)(v[0] - (float)hi[0]), (half_t)(v[1] - (float)hi[1]),
+               (half_t)(v[2] - (float)hi[2]), (half_t)(v[3] - (float)hi[3])};
 }
 
 struct HybridArgs {
     const half_t *dk, *dv, *lk, *rk, *lv, *rv;
     const int32_t* table;
     const int32_t* lens;
-    const float* q;       // [B][Hq][D]
-    float* part;          // [B][Hq][n_split][D + 2]
-    int H, G, P, sink, window, rkk, rvv, max_pages, n_split, pps;
+    const float* q;       // [B][Hq][128]
+    float* part;          // [B][Hq][n_split][128 + 2]
+    int B, H, G, sink, window, rkk, rvv, max_pages, n_split, pps, n_waves;
     float qscale;         // sm_scale * log2(e)
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void hybrid_decode(const HybridArgs a) {
-    static_assert(D == 128, "head_dim 128");
-    constexpr int P = 32;
-    __shared__ float wst[4][4][D + 2];
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int hh = l >> 4, sub = l & 15;
-    const bool head_ok = hh < a.G;
+// Operands of one factored page for this lane (NK / NV: 16-rank blocks of the
+// key / value factors).
+template <int NK, int NV>
+struct FPage {
+    half8 rk[NK][4];      // R_K[16 rb + c][32 s + 8 g + 0..7]
+    half4 lk[2][NK];      // L_K[16 tb + c][16 rb + 4 g + 0..3]
+    half4 lv[2][NV];      // L_V^T[16 rb + c][16 tb + 4 g + 0..3]
+    half4 rv[8][NV];      // R_V^T[16 mb + c][16 rb + 4 g + 0..3]
+};
+
+template <int NK, int NV>
+__global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const HybridArgs a) {
+    constexpr int D = 128, P = 32;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), l = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + w;
+    if (gw >= a.n_waves) return;
+    const int split = gw % a.n_split, bh = gw / a.n_split, h = bh % a.H, b = bh / a.H;
+    const int c = l & 15, g = l >> 4;
     const int Hq = a.H * a.G;
-    const int len = min(a.lens[b], a.max_pages * 32);
+    const int len = min(a.lens[b], a.max_pages * P);
     const int npg = (len + P - 1) / P;
     const int p_begin = split * a.pps;
     const int p_end = min(npg, p_begin + a.pps);
-    const long bh = (long)b * a.H + h;
-    const int j = h * a.G + (head_ok ? hh : 0);
+    const int nd = a.sink + a.window;
 
-    float qv[8];
+    // this range's page-table entries, one per lane; factored / dense masks
+    const int my_pg = p_begin + l;
+    int entry = LRKV_PAGE_EMPTY;
+    if (my_pg < p_end) entry = a.table[(long)bh * a.max_pages + my_pg];
+    const bool fac = my_pg < p_end && entry >= 0 && entry < a.max_pages;
+    const bool den = my_pg < p_end && entry < 0 && entry != LRKV_PAGE_EMPTY && -1 - entry < nd;
+    uint64_t fmask = __builtin_amdgcn_ballot_w64(fac);
+    uint64_t dmask = __builtin_amdgcn_ballot_w64(den);
+
+    // queries of the KV head's G query heads (zero columns past G), hi + lo
+    half8 qh[4], ql[4];
     {
-        const float* qp = a.q + ((long)b * Hq + j) * D + 8 * sub;
+        const float* qs = a.q + ((long)b * Hq + h * a.G + (c < a.G ? c : 0)) * D;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = qp[e] * a.qscale;
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = c < a.G ? qs[32 * s + 8 * g + j] * a.qscale : 0.0f;
+                qh[s][j] = (half_t)v;
+                ql[s][j] = (half_t)(v - (float)qh[s][j]);
+            }
     }
-    float m_run = -INFINITY, l_run = 0.0f, o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
 
-    for (int pg = p_begin + w; pg < p_end; pg += 4) {
-        const int entry = a.table[bh * a.max_pages + pg];
-        const int ntok = min(P, len - pg * P);
-        // pages never written (or out of range) are skipped
-        if (entry >= a.max_pages || (entry < 0 && -1 - (long)entry >= a.sink + a.window)) continue;
-        float s2[2];                          // tokens sub and sub + 16
-        float alpha, pv[2];
-        if (entry >= 0) {
-            // ---- factored page: u = q R_K^T (rank values), s = u L_K^T
-            const half_t* Rk = a.rk + ((bh * a.max_pages + entry) * a.rkk) * D;
-            const half_t* Lk = a.lk + ((bh * a.max_pages + entry) * P) * a.rkk;
-            float s_a = 0.0f, s_b = 0.0f;
-            for (int k = 0; k < a.rkk; ++k) {
-                float r8[8];
-                load8(Rk + (long)k * D + 8 * sub, r8);
-                float uk = 0.0f;
+    const int rk = a.rkk, rv = a.rvv;
+    const long bhp = (long)bh * a.max_pages;
+    const rsrc_t rs_rk = make_rs(a.rk + bhp * rk * D, (uint32_t)(a.max_pages * rk * D * 2));
+    const rsrc_t rs_lk = make_rs(a.lk + bhp * P * rk, (uint32_t)(a.max_pages * P * rk * 2));
+    const rsrc_t rs_lv = make_rs(a.lv + bhp * P * rv, (uint32_t)(a.max_pages * P * rv * 2));
+    const rsrc_t rs_rv = make_rs(a.rv + bhp * rv * D, (uint32_t)(a.max_pages * rv * D * 2));
+
+    // per-lane offsets inside a page (kOff: masked lane), added to the page base
+    uint32_t o_rk[NK], o_lk[NK], o_lv[NV], o_rv[NV];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) uk = fmaf(qv[e], r8[e], uk);
-                uk = row_sum16(uk);
-                s_a = fmaf(uk, (float)Lk[sub * a.rkk + k], s_a);
-                s_b = fmaf(uk, (float)Lk[(sub + 16) * a.rkk + k], s_b);
+    for (int rb = 0; rb < NK; ++rb) {
+        o_rk[rb] = 16 * rb + c < rk ? ((16 * rb + c) * D + 8 * g) * 2 : kOff;
+        o_lk[rb] = 16 * rb + 4 * g < rk ? (c * rk + 16 * rb + 4 * g) * 2 : kOff;
+    }
+#pragma unroll
+    for (int rb = 0; rb < NV; ++rb) {
+        o_lv[rb] = 16 * rb + c < rv ? ((16 * rb + c) * P + 4 * g) * 2 : kOff;
+        o_rv[rb] = 16 * rb + 4 * g < rv ? (c * rv + 16 * rb + 4 * g) * 2 : kOff;
+    }
+
+    // Loads of the next factored page (its bit leaves `mask`); with none left,
+    // every load reads past the buffers (zeros), so the load count per page is
+    // fixed.
+    auto fetch = [&](FPage<NK, NV>& f, uint64_t& mask) __attribute__((always_inline)) {
+        uint32_t slot = 0, none = kOff;
+        if (mask) {
+            const int bit = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            slot = (uint32_t)__builtin_amdgcn_readlane(entry, bit);
+            none = 0;
+        }
+#pragma unroll
+        for (int rb = 0; rb < NK; ++rb) {
+            const uint32_t base = none | (slot * rk * D * 2);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) f.rk[rb][s] = ld8(rs_rk, (base + o_rk[rb] + 64 * s) | (o_rk[rb] & kOff));
+            const uint32_t lbase = none | (slot * P * rk * 2);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) f.lk[tb][rb] = ld4(rs_lk, (lbase + o_lk[rb] + 32 * rk * tb) | (o_lk[rb] & kOff));
+        }
+#pragma unroll
+        for (int rb = 0; rb < NV; ++rb) {
+            const uint32_t lbase = none | (slot * P * rv * 2);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) f.lv[tb][rb] = ld4(rs_lv, (lbase + o_lv[rb] + 32 * tb) | (o_lv[rb] & kOff));
+            const uint32_t base = none | (slot * rv * D * 2);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) f.rv[mb][rb] = ld4(rs_rv, (base + o_rv[rb] + 32 * rv * mb) | (o_rv[rb] & kOff));
+        }
+    };
+
+    float m_run = -INFINITY, l_lane = 0.0f;
+    floatx4 o[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) o[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Online softmax of one page's scores (lane: head c, tokens 16 tb + 4 g + i;
+    // tokens >= ntok masked); returns p as the next MFMA's B operand.
+    auto softmax = [&](const floatx4* S, int ntok, half4* pb) __attribute__((always_inline)) {
+        float sv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sv[k] = S[k >> 2][k & 3];
+        if (ntok < P) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (16 * (k >> 2) + 4 * g + (k & 3) >= ntok) sv[k] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx = xg_max(mx);
+        const float mn = fmaxf(m_run, mx);
+        // rescale only when some head's running max moved (rare after the first pages)
+        if (__builtin_amdgcn_ballot_w64(mn > m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+            l_lane *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+        }
+        m_run = mn;
+        float pr[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(sv[k] - mn);
+        l_lane += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+            pb[tb] = half4{(half_t)pr[4 * tb], (half_t)pr[4 * tb + 1], (half_t)pr[4 * tb + 2], (half_t)pr[4 * tb + 3]};
+    };
+
+    auto factored = [&](const FPage<NK, NV>& f, int ntok) __attribute__((always_inline)) {
+        half4 uh[NK], ul[NK];
+#pragma unroll
+        for (int rb = 0; rb < NK; ++rb) {
+            floatx4 u = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                u = mfma16(f.rk[rb][s], qh[s], u);
+                u = mfma16(f.rk[rb][s], ql[s], u);
             }
-            s2[0] = sub < ntok ? s_a : -INFINITY;
-            s2[1] = sub + 16 < ntok ? s_b : -INFINITY;
-            const float mt = row_max16(fmaxf(s2[0], s2[1]));
-            const float mn = fmaxf(m_run, mt);
-            alpha = exp2f(m_run - mn);
-            pv[0] = exp2f(s2[0] - mn);
-            pv[1] = exp2f(s2[1] - mn);
-            l_run = fmaf(l_run, alpha, row_sum16(pv[0] + pv[1]));
-            m_run = mn;
-            // ---- values: w = p L_V (rank values), o = o alpha + w R_V
-            const half_t* Lv = a.lv + ((bh * a.max_pages + entry) * P) * a.rvv;
-            const half_t* Rv = a.rv + ((bh * a.max_pages + entry) * a.rvv) * D;
+            split4(u, uh[rb], ul[rb]);
+        }
+        floatx4 S[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= alpha;
-            for (int k = 0; k < a.rvv; ++k) {
-                float wk = pv[0] * (float)Lv[sub * a.rvv + k] + pv[1] * (float)Lv[(sub + 16) * a.rvv + k];
-                wk = row_sum16(wk);
-                float r8[8];
-                load8(Rv + (long)k * D + 8 * sub, r8);
+        for (int tb = 0; tb < 2; ++tb) {
+            S[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = fmaf(wk, r8[e], o[e]);
+            for (int rb = 0; rb < NK; ++rb) {
+                S[tb] = mfma16k16(f.lk[tb][rb], uh[rb], S[tb]);
+                S[tb] = mfma16k16(f.lk[tb][rb], ul[rb], S[tb]);
             }
-        } else {
-            // ---- dense page: scores against K rows, then p V
-            const int slot = -1 - entry;
-            const half_t* Kp = a.dk + (bh * (a.sink + a.window) + slot) * P * D;
-            const half_t* Vp = a.dv + (bh * (a.sink + a.window) + slot) * P * D;
-            float my_s[2] = {-INFINITY, -INFINITY};
-            for (int t = 0; t < ntok; ++t) {
-                float k8[8];
-                load8(Kp + (long)t * D + 8 * sub, k8);
-                float st = 0.0f;
+        }
+        half4 pb[2];
+        softmax(S, ntok, pb);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) st = fmaf(qv[e], k8[e], st);
-                st = row_sum16(st);
-                if (t == sub) my_s[0] = st;
-                if (t == sub + 16) my_s[1] = st;
-            }
-            const float mt = row_max16(fmaxf(my_s[0], my_s[1]));
-            const float mn = fmaxf(m_run, mt);
-            alpha = exp2f(m_run - mn);
-            pv[0] = exp2f(my_s[0] - mn);
-            pv[1] = exp2f(my_s[1] - mn);
-            l_run = fmaf(l_run, alpha, row_sum16(pv[0] + pv[1]));
-            m_run = mn;
+        for (int rb = 0; rb < NV; ++rb) {
+            floatx4 wt = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= alpha;
-            for (int t = 0; t < ntok; ++t) {
-                // p of token t lives in lane (t % 16) of this row, slot t / 16
-                const float mine = t < 16 ? pv[0] : pv[1];
-                const float pt = __shfl(mine, (l & ~15) | (t & 15), kWave);
-                float v8[8];
-                load8(Vp + (long)t * D + 8 * sub, v8);
+            for (int tb = 0; tb < 2; ++tb) wt = mfma16k16(f.lv[tb][rb], pb[tb], wt);
+            const half4 wb = to_half4(wt);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = fmaf(pt, v8[e], o[e]);
-            }
+            for (int mb = 0; mb < 8; ++mb) o[mb] = mfma16k16(f.rv[mb][rb], wb, o[mb]);
+        }
+    };
+
+    // ---- factored pages, three register buffers
+    {
+        uint64_t fetch_mask = fmask, run_mask = fmask;
+        auto next_ntok = [&]() __attribute__((always_inline)) {
+            const int bit = __builtin_ctzll(run_mask);
+            run_mask &= run_mask - 1;
+            return min(P, len - (p_begin + bit) * P);
+        };
+        FPage<NK, NV> f0, f1, f2;
+        fetch(f0, fetch_mask);
+        fetch(f1, fetch_mask);
+        while (run_mask) {
+            fetch(f2, fetch_mask);
+            factored(f0, next_ntok());
+            if (!run_mask) break;
+            fetch(f0, fetch_mask);
+            factored(f1, next_ntok());
+            if (!run_mask) break;
+            fetch(f1, fetch_mask);
+            factored(f2, next_ntok());
         }
     }
 
-    if (head_ok) {
-        if (sub == 0) { wst[w][hh][0] = m_run; wst[w][hh][1] = l_run; }
+    // ---- dense pages: K [P][d], V^T [d][P] in their slots
+    while (dmask) {
+        const int bit = __builtin_ctzll(dmask);
+        dmask &= dmask - 1;
+        const int slot = -1 - __builtin_amdgcn_readlane(entry, bit);
+        const int ntok = min(P, len - (p_begin + bit) * P);
+        const long sb = (long)bh * nd + slot;
+        const rsrc_t rs_k = make_rs(a.dk + sb * P * D, P * D * 2);
+        const rsrc_t rs_v = make_rs(a.dv + sb * P * D, P * D * 2);
+        half8 kf[2][4];
+        half4 vf[8][2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wst[w][hh][2 + 8 * sub + e] = o[e];
-    }
-    __syncthreads();
-    float* part = a.part + ((long)(b * Hq + h * a.G) * a.n_split + split) * (D + 2);
-    const long hstride = (long)a.n_split * (D + 2);
-    for (int e = tid; e < a.G * (D + 2); e += 256) {
-        const int g = e / (D + 2), c = e % (D + 2);
-        float mx = -INFINITY;
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) mx = fmaxf(mx, wst[ww][g][0]);
-        float val = mx;
-        if (c > 0) {
-            val = 0.0f;
+            for (int s = 0; s < 4; ++s) kf[tb][s] = ld8(rs_k, ((16 * tb + c) * D + 32 * s + 8 * g) * 2);
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww) {
-                const float m = wst[ww][g][0];
-                if (m != -INFINITY) val = fmaf(exp2f(m - mx), wst[ww][g][c], val);
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) vf[mb][tb] = ld4(rs_v, ((16 * mb + c) * P + 16 * tb + 4 * g) * 2);
+        floatx4 S[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            S[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                S[tb] = mfma16(kf[tb][s], qh[s], S[tb]);
+                S[tb] = mfma16(kf[tb][s], ql[s], S[tb]);
             }
         }
-        part[g * hstride + c] = val;
+        half4 pb[2];
+        softmax(S, ntok, pb);
+        if (ntok < P) {
+            // rows past the page's last token may hold anything; their p is zero
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * tb + 4 * g + i >= ntok) vf[mb][tb][i] = (half_t)0.0f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) o[mb] = mfma16k16(vf[mb][tb], pb[tb], o[mb]);
     }
+
+    // ---- chunk state of the G heads: (m, l, unnormalised o)
+    const float l_sum = xg_sum(l_lane);
+    if (c < a.G) {
+        float* ph = a.part + ((long)(b * Hq + h * a.G + c) * a.n_split + split) * (D + 2);
+        if (g == 0) {
+            ph[0] = m_run;
+            ph[1] = l_sum;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ph[2 + 16 * mb + 4 * g + i] = o[mb][i];
+    }
+}
+
+template <int NK, int NV>
+void launch_hybrid(const HybridArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((hybrid_decode<NK, NV>), dim3((a.n_waves + 3) / 4), dim3(256), 0, st, a);
 }
 
 }  // namespace
@@ -197,11 +354,16 @@ int32_t launch_decode_hybrid(int phases, const lrkv_paged_cache* c, const float*
     float* part = (float*)((char*)ws + w.part_off);
     HybridArgs a{(const half_t*)c->dense_k, (const half_t*)c->dense_v, (const half_t*)c->lk,
                  (const half_t*)c->rk, (const half_t*)c->lv, (const half_t*)c->rv, c->page_table,
-                 c->lens, q, part, c->kv_heads, c->q_per_kv, c->page_size, c->sink_pages,
+                 c->lens, q, part, c->batch, c->kv_heads, c->q_per_kv, c->sink_pages,
                  c->window_pages, c->rank_k, c->rank_v, c->max_pages, w.n_split,
-                 w.pages_per_split, sm_scale * kLog2e};
-    if (phases & kPhasePartials)
-        hipLaunchKernelGGL(hybrid_decode<128>, dim3(w.n_split, c->kv_heads, c->batch), dim3(256), 0, st, a);
+                 w.pages_per_split, c->batch * c->kv_heads * w.n_split, sm_scale * kLog2e};
+    if (phases & kPhasePartials) {
+        const bool k2 = c->rank_k > 16, v2 = c->rank_v > 16;
+        if (!k2 && !v2) launch_hybrid<1, 1>(a, st);
+        else if (!k2) launch_hybrid<1, 2>(a, st);
+        else if (!v2) launch_hybrid<2, 1>(a, st);
+        else launch_hybrid<2, 2>(a, st);
+    }
     if (phases & kPhaseMerge)
         launch_merge(part, out, c->batch * c->kv_heads * c->q_per_kv, w.n_split, c->head_dim, st);
     return last_launch_status();

@@ -12,7 +12,8 @@
 //      matrix). A pair is skipped when |g_pq| <= 1e-6 trace(G); the sweeps stop
 //      when a sweep skips every pair or after max_sweeps.
 //   3. Eigenvalues sorted descending (ties: lower index first); L = the first r
-//      eigenvectors rounded to fp16, R = L^T X accumulated in fp32, stored fp16.
+//      eigenvectors rounded to fp16, R = L^T X accumulated in fp32, stored fp16
+//      (value pages transposed: L^T and R^T, the layout the decode reads).
 // The page-table entries are switched to "factored" by a second kernel so that
 // the K and V waves of one page never race on them.
 #include "common.h"
@@ -31,10 +32,12 @@ struct FactorArgs {
 };
 
 // Resolves a (b, h, page) triple: returns false when it must be skipped; sets the
-// source row pointer of the page's K (or V) rows otherwise.
+// source pointer of the page's K (or V) otherwise. `dim_major`: the source is
+// a dense slot's values, stored [d][P].
 template <int D>
 __device__ bool resolve(const FactorArgs& a, int idx, bool is_v, int& b, int& h, int& pg,
-                        const half_t*& X) {
+                        const half_t*& X, bool& dim_major) {
+    dim_major = false;
     b = a.pages[3 * idx + 0];
     h = a.pages[3 * idx + 1];
     pg = a.pages[3 * idx + 2];
@@ -50,6 +53,7 @@ __device__ bool resolve(const FactorArgs& a, int idx, bool is_v, int& b, int& h,
     const int slot = -1 - entry;
     if (slot >= a.sink + a.window) return false;
     X = (is_v ? a.dv : a.dk) + ((bh * (a.sink + a.window) + slot) * a.P) * D;
+    dim_major = is_v;
     return true;
 }
 
@@ -76,17 +80,33 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
     const bool is_v = m & 1;
     int b, h, pg;
     const half_t* X;
-    if (!resolve<D>(a, idx, is_v, b, h, pg, X)) return;
+    bool dim_major;
+    if (!resolve<D>(a, idx, is_v, b, h, pg, X, dim_major)) return;
     const int r = is_v ? a.rank_v : a.rank_k;
     float (*G)[P + 1] = Gs[w];
     float (*V)[P + 1] = Vs[w];
 
     // ---- Gram matrix on the MFMA; X kept in LDS for R = L^T X
     floatx16 acc = floatx16{};
+    if (dim_major) {
+        // X^T [D][P] in global memory: transpose into Xs first
+        for (int e = l; e < D * P / 8; e += 64) {
+            const int dd = e / (P / 8), t8 = e % (P / 8);
+            const half8 x = *reinterpret_cast<const half8*>(X + (long)dd * P + 8 * t8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) Xs[w][8 * t8 + j][dd] = x[j];
+        }
+        wave_sync_lds();
+    }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-        const half8 x = *reinterpret_cast<const half8*>(X + (long)(l & 31) * D + 16 * kk + 8 * (l >> 5));
-        *reinterpret_cast<half8*>(&Xs[w][l & 31][16 * kk + 8 * (l >> 5)]) = x;
+        half8 x;
+        if (dim_major) {
+            x = *reinterpret_cast<const half8*>(&Xs[w][l & 31][16 * kk + 8 * (l >> 5)]);
+        } else {
+            x = *reinterpret_cast<const half8*>(X + (long)(l & 31) * D + 16 * kk + 8 * (l >> 5));
+            *reinterpret_cast<half8*>(&Xs[w][l & 31][16 * kk + 8 * (l >> 5)]) = x;
+        }
         acc = mfma32(x, x, acc);
     }
 #pragma unroll
@@ -165,9 +185,10 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
     const long bh = (long)b * a.H + h;
     half_t* Lo = (is_v ? a.lv : a.lk) + (bh * a.max_pages + pg) * P * r;
     half_t* Ro = (is_v ? a.rv : a.rk) + (bh * a.max_pages + pg) * (long)r * D;
+    // keys: L [P][r], R [r][D]; values transposed: L^T [r][P], R^T [D][r]
     for (int e = l; e < P * r; e += 64) {
         const int t = e / r, k = e % r;
-        Lo[e] = (half_t)V[t][order[w][k]];
+        Lo[is_v ? k * P + t : e] = (half_t)V[t][order[w][k]];
     }
     // R[k][d] = sum_t fp16(L[t][k]) X[t][d]
     for (int k = 0; k < r; ++k) {
@@ -176,7 +197,7 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
             float s = 0.0f;
 #pragma unroll 8
             for (int t = 0; t < P; ++t) s = fmaf((float)(half_t)V[t][col], (float)Xs[w][t][d], s);
-            Ro[(long)k * D + d] = (half_t)s;
+            Ro[is_v ? (long)d * r + k : (long)k * D + d] = (half_t)s;
         }
     }
 }
@@ -186,7 +207,8 @@ __global__ void mark_factored(const FactorArgs a) {
     if (idx >= a.n_pages) return;
     int b, h, pg;
     const half_t* X;
-    if (!resolve<128>(a, idx, false, b, h, pg, X)) return;
+    bool dim_major;
+    if (!resolve<128>(a, idx, false, b, h, pg, X, dim_major)) return;
     a.table[((long)b * a.H + h) * a.max_pages + pg] = pg;
 }
 

@@ -105,6 +105,12 @@ def test_paged_validation(lib):
     assert lib.lrkv_factor_page(ctypes.byref(d), ok, 3, ok, None, 64, 0, None) == L.LRKV_ERR_INVALID_ARG
     bad = _paged(page_size=16)
     assert lib.lrkv_factor_page(ctypes.byref(bad), ok, 3, None, None, 0, 0, None) == L.LRKV_ERR_UNSUPPORTED
+    # ranks must be multiples of 4 (up to 32), at most 16 query heads per KV head
+    for kw in (dict(rank_k=10), dict(rank_v=36), dict(q_per_kv=17), dict(max_pages=65537)):
+        bad = _paged(**kw)
+        assert lib.lrkv_factor_page(ctypes.byref(bad), ok, 3, None, None, 0, 0, None) == L.LRKV_ERR_UNSUPPORTED, kw
+        assert lib.lrkv_decode_workspace_bytes(2, ctypes.byref(bad), 1000, 0) == 0, kw
+    assert lib.lrkv_decode_workspace_bytes(2, ctypes.byref(_paged(q_per_kv=16, rank_k=32, rank_v=4)), 1000, 0) > 0
     need = lib.lrkv_decode_workspace_bytes(2, ctypes.byref(d), 1000, 0)
     assert need > 0
     assert lib.lrkv_decode_attn(2, ctypes.byref(d), ok, ok, None, 0.0, ok, ok, need, 1000, 0, None) == L.LRKV_ERR_INVALID_ARG

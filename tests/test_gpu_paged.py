@@ -49,7 +49,7 @@ def _write_cache_directly(cache, dk, dv, Lk, Rk, Lv, Rv, T):
     npg = (T + P - 1) // P
     table = np.full((B, H, cache.max_pages), -(2 ** 31), np.int32)
     dense_k = np.zeros(tuple(cache.dense_k.shape), np.float16)
-    dense_v = np.zeros_like(dense_k)
+    dense_v = np.zeros(tuple(cache.dense_v.shape), np.float16)
     lk = np.zeros(tuple(cache.lk.shape), np.float16)
     rk = np.zeros(tuple(cache.rk.shape), np.float16)
     lv = np.zeros(tuple(cache.lv.shape), np.float16)
@@ -58,12 +58,14 @@ def _write_cache_directly(cache, dk, dv, Lk, Rk, Lv, Rv, T):
         lo, hi = p * P, min((p + 1) * P, T)
         if cache.sink <= p < npg - cache.window:
             table[:, :, p] = p
-            lk[:, :, p], rk[:, :, p], lv[:, :, p], rv[:, :, p] = Lk[:, :, p], Rk[:, :, p], Lv[:, :, p], Rv[:, :, p]
+            lk[:, :, p], rk[:, :, p] = Lk[:, :, p], Rk[:, :, p]
+            # value-side factors are stored transposed: L_V^T [r][P], R_V^T [d][r]
+            lv[:, :, p], rv[:, :, p] = np.swapaxes(Lv[:, :, p], -1, -2), np.swapaxes(Rv[:, :, p], -1, -2)
         else:
             slot = p if p < cache.sink else cache.sink + (p - cache.sink) % cache.window
             table[:, :, p] = -1 - slot
             dense_k[:, :, slot, :hi - lo] = dk[:, :, lo:hi]
-            dense_v[:, :, slot, :hi - lo] = dv[:, :, lo:hi]
+            dense_v[:, :, slot, :, :hi - lo] = np.swapaxes(dv[:, :, lo:hi], -1, -2)
     for name, arr in (("dense_k", dense_k), ("dense_v", dense_v), ("lk", lk), ("rk", rk), ("lv", lv),
                       ("rv", rv), ("page_table", table)):
         getattr(cache, name).copy_(torch.from_numpy(arr))
@@ -71,18 +73,20 @@ def _write_cache_directly(cache, dk, dv, Lk, Rk, Lv, Rv, T):
     cache.host_lens[:] = T
 
 
-@pytest.mark.parametrize("B,H,G,T,lens_cut", [(2, 2, 4, 32 * 20 + 7, 0), (1, 3, 4, 32 * 9, 0), (2, 2, 2, 100, 0)])
-def test_hybrid_decode_parity(B, H, G, T, lens_cut):
+@pytest.mark.parametrize("B,H,G,T,rk,rv", [(2, 2, 4, 32 * 20 + 7, 12, 12), (1, 3, 4, 32 * 9, 12, 12),
+                                            (2, 2, 2, 100, 12, 12), (1, 2, 8, 32 * 70 + 5, 12, 12),
+                                            (1, 2, 16, 32 * 11 + 31, 16, 32), (2, 1, 4, 32 * 13, 20, 8)])
+def test_hybrid_decode_parity(B, H, G, T, rk, rv):
     R = _R()
-    say(f"hybrid decode parity: B={B} H={H} G={G} T={T}")
-    cache = R.PagedCache(B, H, G, 128, P, 1, 4, 12, 12, max_pages=(T + P - 1) // P + 2)
+    say(f"hybrid decode parity: B={B} H={H} G={G} T={T} rk={rk} rv={rv}")
+    cache = R.PagedCache(B, H, G, 128, P, 1, 4, rk, rv, max_pages=(T + P - 1) // P + 2)
     dense = synth.paged_dense(51, B, H, T, 128)
     npg = (T + P - 1) // P
-    fk = synth.factored_pages(52, B * H * npg, P, 128, 12)
-    fv = synth.factored_pages(53, B * H * npg, P, 128, 12)
+    fk = synth.factored_pages(52, B * H * npg, P, 128, rk)
+    fv = synth.factored_pages(53, B * H * npg, P, 128, rv)
     shp = lambda a, last: a.reshape((B, H, npg) + last)
-    Lk, Rk = shp(fk["L"], (P, 12)), shp(fk["R"], (12, 128))
-    Lv, Rv = shp(fv["L"], (P, 12)), shp(fv["R"], (12, 128))
+    Lk, Rk = shp(fk["L"], (P, rk)), shp(fk["R"], (rk, 128))
+    Lv, Rv = shp(fv["L"], (P, rv)), shp(fv["R"], (rv, 128))
     _write_cache_directly(cache, dense["k"], dense["v"], Lk, Rk, Lv, Rv, T)
     q = synth.queries(54, B, H * G, 128, 2.0)
     got = cache.decode(to_dev(q))
@@ -125,7 +129,8 @@ def test_prefill_factorisation(noise, rank):
     npg = len(expect)
     assert np.array_equal(table[:, :, :npg], np.broadcast_to(expect, (B, H, npg)))
     lk, rk = cache.lk.cpu().numpy().astype(np.float64), cache.rk.cpu().numpy().astype(np.float64)
-    lv, rv = cache.lv.cpu().numpy().astype(np.float64), cache.rv.cpu().numpy().astype(np.float64)
+    lv = np.swapaxes(cache.lv.cpu().numpy().astype(np.float64), -1, -2)
+    rv = np.swapaxes(cache.rv.cpu().numpy().astype(np.float64), -1, -2)
     for b in range(B):
         for h in range(H):
             for p in np.nonzero(expect >= 0)[0]:
@@ -136,10 +141,12 @@ def test_prefill_factorisation(noise, rank):
                     assert err <= 1.01 * eps + 1e-3 * np.linalg.norm(Xp), (b, h, p, err, eps)
     # dense slots hold the sink page and the window pages
     dk = cache.dense_k.cpu().numpy()
-    assert np.array_equal(dk[:, :, 0], dense["k"][:, :, :P])
+    dv = np.swapaxes(cache.dense_v.cpu().numpy(), -1, -2)
     last = npg - 1
     slot = 1 + (last - 1) % 4
-    assert np.array_equal(dk[:, :, slot, :T - last * P], dense["k"][:, :, last * P:T])
+    for got, src in ((dk, dense["k"]), (dv, dense["v"])):
+        assert np.array_equal(got[:, :, 0], src[:, :, :P])
+        assert np.array_equal(got[:, :, slot, :T - last * P], src[:, :, last * P:T])
 
 
 def test_decode_loop_against_oracle():
@@ -180,8 +187,10 @@ def test_hybrid_split_independence():
     cache.prefill(to_dev(dense["k"]), to_dev(dense["v"]))
     q = to_dev(synth.queries(60, B, H * G, 128, 2.0))
     outs = [cache.decode(q, n_split=n).cpu().numpy() for n in (1, 5, 40, 0)]
+    # p and w = p L_V enter the value products in fp16, rounded relative to each
+    # chunk's own running max, so chunkings differ by a few fp16 roundings
     for o in outs[1:]:
-        assert rel_l2(o, outs[0]).max() <= 1e-5
+        assert rel_l2(o, outs[0]).max() <= 2 * 2.0 ** -11
 
 
 def test_hybrid_workload_sampled():
