@@ -5,12 +5,14 @@
 // vectors of X, so L = Q_r and R = Q_r^T X are the truncated-SVD factors
 // (R = S_r W_r^T). Pages have one shape, so many are factored in one launch.
 //
-// One wave per page matrix (K or V of one page):
+// One single-wave workgroup per page matrix (K or V of one page):
 //   1. X (fp16) -> G on the 32x32x16 MFMA (A and B fragments are the same rows).
-//   2. Cyclic Jacobi on G in LDS, fp32, round-robin ordering: each round rotates
-//      16 disjoint index pairs at once (rows, then columns, then the eigenvector
-//      matrix). A pair is skipped when |g_pq| <= 1e-6 trace(G); the sweeps stop
-//      when a sweep skips every pair or after max_sweeps.
+//   2. Cyclic Jacobi on G in LDS, fp32, round-robin (circle-method) ordering:
+//      each round rotates 16 disjoint index pairs at once, applied as one pass
+//      of 2x2 block updates (rows and columns together) plus the eigenvector
+//      columns, written to the next round's positions in a second buffer. A
+//      pair is skipped when |g_pq| <= 1e-6 trace(G); the sweeps stop when a
+//      sweep skips every pair or after max_sweeps.
 //   3. Eigenvalues sorted descending (ties: lower index first); L = the first r
 //      eigenvectors rounded to fp16, R = L^T X accumulated in fp32, stored fp16
 //      (value pages transposed: L^T and R^T, the layout the decode reads).
@@ -63,18 +65,30 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
-    constexpr int P = 32;
-    __shared__ float Gs[4][P][P + 1];
-    __shared__ float Vs[4][P][P + 1];
-    __shared__ half_t Xs[4][P][D + 8];
-    __shared__ float rot[4][16][2];
-    __shared__ int rpq[4][16][2];
-    __shared__ int order[4][P];
+// Circle-method position map of the round-robin ordering: positions 2k and
+// 2k+1 hold the pair rotated in a round; after the round, the element at
+// position x moves to sigma(x). Position 0 stays; the other 31 positions form
+// one cycle (top row 2 -> 4 -> ... -> 30, bottom row 31 -> 29 -> ... -> 1,
+// 30 -> 31, 1 -> 2), so any two indices share a pair exactly once in 31
+// rounds and the positions are the identity again after each sweep.
+__device__ __forceinline__ int sigma(int x) {
+    if (x == 0) return 0;
+    if (x == 1) return 2;
+    if (x & 1) return x - 2;
+    return x == 30 ? 31 : x + 2;
+}
 
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int m = blockIdx.x * 4 + w;
+template <int D>
+__global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
+    constexpr int P = 32, LD = P + 1;
+    __shared__ float Gb[2][P][LD];     // G, double-buffered across rounds
+    __shared__ float Vb[2][P][LD];     // eigenvectors (columns), likewise
+    __shared__ half_t Xs[P][D + 8];
+    __shared__ float rot[16][2];
+    __shared__ int order[P];
+
+    const int l = threadIdx.x;
+    const int m = blockIdx.x;
     if (m >= 2 * a.n_pages) return;
     const int idx = m >> 1;
     const bool is_v = m & 1;
@@ -83,8 +97,6 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
     bool dim_major;
     if (!resolve<D>(a, idx, is_v, b, h, pg, X, dim_major)) return;
     const int r = is_v ? a.rank_v : a.rank_k;
-    float (*G)[P + 1] = Gs[w];
-    float (*V)[P + 1] = Vs[w];
 
     // ---- Gram matrix on the MFMA; X kept in LDS for R = L^T X
     floatx16 acc = floatx16{};
@@ -94,7 +106,7 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
             const int dd = e / (P / 8), t8 = e % (P / 8);
             const half8 x = *reinterpret_cast<const half8*>(X + (long)dd * P + 8 * t8);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) Xs[w][8 * t8 + j][dd] = x[j];
+            for (int j = 0; j < 8; ++j) Xs[8 * t8 + j][dd] = x[j];
         }
         wave_sync_lds();
     }
@@ -102,73 +114,85 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
     for (int kk = 0; kk < D / 16; ++kk) {
         half8 x;
         if (dim_major) {
-            x = *reinterpret_cast<const half8*>(&Xs[w][l & 31][16 * kk + 8 * (l >> 5)]);
+            x = *reinterpret_cast<const half8*>(&Xs[l & 31][16 * kk + 8 * (l >> 5)]);
         } else {
             x = *reinterpret_cast<const half8*>(X + (long)(l & 31) * D + 16 * kk + 8 * (l >> 5));
-            *reinterpret_cast<half8*>(&Xs[w][l & 31][16 * kk + 8 * (l >> 5)]) = x;
+            *reinterpret_cast<half8*>(&Xs[l & 31][16 * kk + 8 * (l >> 5)]) = x;
         }
         acc = mfma32(x, x, acc);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) G[8 * (i / 4) + 4 * (l >> 5) + (i % 4)][l & 31] = acc[i];
-    for (int e = l; e < P * P; e += 64) V[e / P][e % P] = (e / P == e % P) ? 1.0f : 0.0f;
+    for (int i = 0; i < 16; ++i) Gb[0][8 * (i / 4) + 4 * (l >> 5) + (i % 4)][l & 31] = acc[i];
+    for (int e = l; e < P * P; e += 64) Vb[0][e / P][e % P] = (e / P == e % P) ? 1.0f : 0.0f;
     wave_sync_lds();
-    float tr = l < P ? G[l][l] : 0.0f;
+    float tr = l < P ? Gb[0][l][l] : 0.0f;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o, kWave);
     const float thr = 1e-6f * tr;
 
-    // ---- cyclic Jacobi, round-robin pairs
+    // ---- cyclic Jacobi. Round: lanes k < 16 form the rotation of positions
+    // (2k, 2k+1); then G <- J^T G J and V <- V J in one pass of 2x2 blocks, each
+    // result written at its position for the next round (sigma) in the other
+    // buffer. Lane l owns the blocks (pair a = l / 4) x (pairs 4 (l % 4) + j) and
+    // the eigenvector rows l / 16 + 4 i of pair l % 16: fixed addresses.
+    const int pa = l >> 2, pv = l & 15;
+    const int ra0 = sigma(2 * pa), ra1 = sigma(2 * pa + 1);
+    const int cv0 = sigma(2 * pv), cv1 = sigma(2 * pv + 1);
+    int cur = 0;
     for (int sweep = 0; sweep < a.max_sweeps; ++sweep) {
         int rotated = 0;
         for (int rd = 0; rd < P - 1; ++rd) {
+            float (*G)[LD] = Gb[cur];
+            float (*Gn)[LD] = Gb[cur ^ 1];
+            float (*V)[LD] = Vb[cur];
+            float (*Vn)[LD] = Vb[cur ^ 1];
             if (l < 16) {
-                int p = l == 0 ? P - 1 : (rd + l) % (P - 1);
-                int q = l == 0 ? rd : (rd + (P - 1) - l) % (P - 1);
-                if (p > q) { const int t = p; p = q; q = t; }
-                const float apq = G[p][q];
+                const float gpp = G[2 * l][2 * l], gqq = G[2 * l + 1][2 * l + 1], apq = G[2 * l][2 * l + 1];
                 float c = 1.0f, s = 0.0f;
                 if (fabsf(apq) > thr) {
-                    const float tau = (G[q][q] - G[p][p]) / (2.0f * apq);
-                    const float t = copysignf(1.0f, tau) / (fabsf(tau) + sqrtf(fmaf(tau, tau, 1.0f)));
-                    c = 1.0f / sqrtf(fmaf(t, t, 1.0f));
+                    const float tau = (gqq - gpp) * __builtin_amdgcn_rcpf(2.0f * apq);
+                    const float t = copysignf(__builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.0f))), tau);
+                    c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.0f));
                     s = t * c;
                     rotated = 1;
                 }
-                rot[w][l][0] = c;
-                rot[w][l][1] = s;
-                rpq[w][l][0] = p;
-                rpq[w][l][1] = q;
+                rot[l][0] = c;
+                rot[l][1] = s;
             }
             wave_sync_lds();
-            // rows: G <- J^T G
+            const float ca = rot[pa][0], sa = rot[pa][1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int pb = 4 * (l & 3) + j;
+                const float cb = rot[pb][0], sb = rot[pb][1];
+                const float g00 = G[2 * pa][2 * pb], g01 = G[2 * pa][2 * pb + 1];
+                const float g10 = G[2 * pa + 1][2 * pb], g11 = G[2 * pa + 1][2 * pb + 1];
+                const float r00 = fmaf(ca, g00, -sa * g10), r01 = fmaf(ca, g01, -sa * g11);
+                const float r10 = fmaf(sa, g00, ca * g10), r11 = fmaf(sa, g01, ca * g11);
+                float n01 = fmaf(sb, r00, cb * r01), n10 = fmaf(cb, r10, -sb * r11);
+                if (pa == pb && sa != 0.0f) n01 = n10 = 0.0f;   // the pair's own entry is annihilated
+                const int cb0 = sigma(2 * pb), cb1 = sigma(2 * pb + 1);
+                Gn[ra0][cb0] = fmaf(cb, r00, -sb * r01);
+                Gn[ra0][cb1] = n01;
+                Gn[ra1][cb0] = n10;
+                Gn[ra1][cb1] = fmaf(sb, r10, cb * r11);
+            }
+            const float cv = rot[pv][0], sv = rot[pv][1];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int item = l + 64 * i, k = item >> 5, col = item & 31;
-                const int p = rpq[w][k][0], q = rpq[w][k][1];
-                const float c = rot[w][k][0], s = rot[w][k][1];
-                const float gp = G[p][col], gq = G[q][col];
-                G[p][col] = fmaf(c, gp, -s * gq);
-                G[q][col] = fmaf(s, gp, c * gq);
+                const int row = (l >> 4) + 4 * i;
+                const float vp = V[row][2 * pv], vq = V[row][2 * pv + 1];
+                Vn[row][cv0] = fmaf(cv, vp, -sv * vq);
+                Vn[row][cv1] = fmaf(sv, vp, cv * vq);
             }
             wave_sync_lds();
-            // columns: G <- G J, V <- V J
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int item = l + 64 * i, k = item >> 5, row = item & 31;
-                const int p = rpq[w][k][0], q = rpq[w][k][1];
-                const float c = rot[w][k][0], s = rot[w][k][1];
-                const float gp = G[row][p], gq = G[row][q];
-                G[row][p] = fmaf(c, gp, -s * gq);
-                G[row][q] = fmaf(s, gp, c * gq);
-                const float vp = V[row][p], vq = V[row][q];
-                V[row][p] = fmaf(c, vp, -s * vq);
-                V[row][q] = fmaf(s, vp, c * vq);
-            }
-            wave_sync_lds();
+            cur ^= 1;
         }
         if (!__any(rotated)) break;
     }
+    float (*G)[LD] = Gb[cur];
+    float (*V)[LD] = Vb[cur];
+    float (*Ls)[LD] = Gb[cur ^ 1];     // free now: L^T [k][t] as rounded to fp16
 
     // ---- descending eigen-order, ties towards the lower index
     if (l < P) {
@@ -178,7 +202,7 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
             const float lj = G[j][j];
             rank += (lj > li) || (lj == li && j < l);
         }
-        order[w][rank] = l;
+        order[rank] = l;
     }
     wave_sync_lds();
 
@@ -188,16 +212,32 @@ __global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
     // keys: L [P][r], R [r][D]; values transposed: L^T [r][P], R^T [D][r]
     for (int e = l; e < P * r; e += 64) {
         const int t = e / r, k = e % r;
-        Lo[is_v ? k * P + t : e] = (half_t)V[t][order[w][k]];
+        const half_t v = (half_t)V[t][order[k]];
+        Lo[is_v ? k * P + t : e] = v;
+        Ls[k][t] = (float)v;
     }
-    // R[k][d] = sum_t fp16(L[t][k]) X[t][d]
+    wave_sync_lds();
+    // R[k][d] = sum_t fp16(L[t][k]) X[t][d]: lane l owns dims l and l + 64
+    float x0[P], x1[P];
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+        x0[t] = (float)Xs[t][l];
+        x1[t] = (float)Xs[t][l + 64];
+    }
     for (int k = 0; k < r; ++k) {
-        const int col = order[w][k];
-        for (int d = l; d < D; d += 64) {
-            float s = 0.0f;
-#pragma unroll 8
-            for (int t = 0; t < P; ++t) s = fmaf((float)(half_t)V[t][col], (float)Xs[w][t][d], s);
-            Ro[is_v ? (long)d * r + k : (long)k * D + d] = (half_t)s;
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int t = 0; t < P; ++t) {
+            const float lt = Ls[k][t];
+            s0 = fmaf(lt, x0[t], s0);
+            s1 = fmaf(lt, x1[t], s1);
+        }
+        if (is_v) {
+            Ro[(long)l * r + k] = (half_t)s0;
+            Ro[(long)(l + 64) * r + k] = (half_t)s1;
+        } else {
+            Ro[(long)k * D + l] = (half_t)s0;
+            Ro[(long)k * D + l + 64] = (half_t)s1;
         }
     }
 }
@@ -222,7 +262,7 @@ int32_t launch_factor_page(const lrkv_paged_cache* c, const int32_t* pages, int 
                  (half_t*)c->lk, (half_t*)c->rk, (half_t*)c->lv, (half_t*)c->rv, c->page_table,
                  pages, n_pages, c->batch, c->kv_heads, c->page_size, c->sink_pages,
                  c->window_pages, c->max_pages, c->rank_k, c->rank_v, src_len, max_sweeps};
-    hipLaunchKernelGGL(factor_pages<128>, dim3((2 * n_pages + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(factor_pages<128>, dim3(2 * n_pages), dim3(64), 0, st, a);
     hipLaunchKernelGGL(mark_factored, dim3((n_pages + 255) / 256), dim3(256), 0, st, a);
     return last_launch_status();
 }
