@@ -94,6 +94,21 @@ def _row(ms: list, nbytes: float, flops: float = 0.0) -> dict:
     return out
 
 
+def measure_stream_read(torch, lrkv, dev, nbytes: int = 4 << 30, iters: int = 10) -> dict:
+    """The practical HBM read rate on this GPU: lrkv_probe_stream_read over a 4 GiB
+    buffer (16x the last-level cache), median of `iters` launches."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    blocks = 8192
+    out = torch.empty(blocks, dtype=torch.int32, device=dev)
+    ms = _time(torch, lambda: lrkv.probe_stream_read(buf, out, blocks), iters)
+    del buf, out
+    m = float(np.median(ms))
+    gbs = nbytes / (m * 1e-3) / 1e9
+    return {"GB_s": round(gbs, 1), "bytes": nbytes, "us_median": round(m * 1e3, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def measure_rows(torch, lrkv, dev, iters: int = 20) -> dict:
     """The other hot-path rows at their workloads (one decode_attn call each, merge
     included; factorisation batches). Seeded synthetic inputs generated on the GPU:
@@ -366,11 +381,19 @@ def main() -> int:
             "output_finite": ok,
         },
     }
+    del reps, ws
+    torch.cuda.empty_cache()
+    log("bench: streaming-read reference")
+    sr = measure_stream_read(torch, lrkv, dev)
+    result["detail"]["stream_read"] = sr
+    result["detail"]["partials_frac_stream_read"] = round(achieved / sr["GB_s"], 4)
     if not args.no_rows:
         log("bench: timing the other hot-path rows")
-        del reps, ws
-        torch.cuda.empty_cache()
-        result["detail"]["rows"] = measure_rows(torch, lrkv, dev)
+        rows = measure_rows(torch, lrkv, dev)
+        for r in rows.values():
+            if "GB_s" in r:
+                r["frac_stream_read"] = round(r["GB_s"] / sr["GB_s"], 4)
+        result["detail"]["rows"] = rows
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(T)

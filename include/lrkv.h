@@ -275,6 +275,18 @@ int32_t lrkv_factor_page(const lrkv_paged_cache *cache, const int32_t *pages, in
 int32_t lrkv_paged_plan(const lrkv_paged_cache *cache, const int32_t *host_lens, int32_t n_new,
                         int32_t *out, int32_t max_out);
 
+/*
+ * Measurement aid, not part of the decode path: reads `bytes` (a multiple of
+ * 16) of device memory `buf` once with a streaming kernel of `blocks`
+ * workgroups (1..65535) and writes one word per workgroup to device `out`
+ * (uint32 [blocks]). Its duration is the practical HBM read rate the decode
+ * kernels are compared against, beside the nominal peak. LRKV_ERR_INVALID_ARG
+ * on a NULL or unaligned buffer, a size not a multiple of 16 or a bad block
+ * count.
+ */
+int32_t lrkv_probe_stream_read(const void *buf, size_t bytes, uint32_t *out, int32_t blocks,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

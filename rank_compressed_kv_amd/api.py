@@ -18,7 +18,7 @@ from ._lib import (BLOCK, FMT_FP16, FMT_INT4_G32, MODE_ABSORBED, MODE_HYBRID_PAG
 
 __all__ = [
     "decode_workspace_bytes", "append_latent", "decode_attn", "decode_prepare", "decode_partials",
-    "merge_partials", "factor_page", "paged_plan",
+    "merge_partials", "factor_page", "paged_plan", "probe_stream_read",
     "LatentCache", "PagedCache", "LrkvError",
     "MODE_ROPE_RECON", "MODE_ABSORBED", "MODE_HYBRID_PAGED", "FMT_FP16", "FMT_INT4_G32",
 ]
@@ -87,6 +87,14 @@ def factor_page(desc, pages, n_pages: int, src_k=None, src_v=None, src_len: int 
                 max_sweeps: int = 0, stream=None) -> None:
     L.check(L.lib().lrkv_factor_page(ctypes.byref(desc), _p(pages), n_pages, _p(src_k), _p(src_v),
                                      src_len, max_sweeps, _stream(stream)), "lrkv_factor_page")
+
+
+def probe_stream_read(buf, out, blocks: int = 4096, stream=None) -> None:
+    """Measurement aid: one streaming read of every byte of device tensor `buf`
+    (out: device uint8/int32 tensor of at least 4 * blocks bytes)."""
+    nbytes = buf.numel() * buf.element_size()
+    L.check(L.lib().lrkv_probe_stream_read(_p(buf), nbytes, _p(out), blocks, _stream(stream)),
+            "lrkv_probe_stream_read")
 
 
 def paged_plan(desc, host_lens: np.ndarray, n_new: int) -> np.ndarray:

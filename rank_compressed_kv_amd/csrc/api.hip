@@ -307,4 +307,10 @@ int32_t lrkv_paged_plan(const lrkv_paged_cache* c, const int32_t* host_lens, int
     return count > 0x7fffffff ? LRKV_ERR_INVALID_ARG : (int32_t)count;
 }
 
+int32_t lrkv_probe_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* stream) {
+    if (!buf || !out || bytes == 0 || (bytes % 16) || (((uintptr_t)buf) & 15) || blocks < 1 || blocks > 65535)
+        return LRKV_ERR_INVALID_ARG;
+    return launch_stream_read(buf, bytes, out, blocks, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -167,3 +167,13 @@ def test_workspace_monotone_in_length(lib):
         n = lib.lrkv_decode_workspace_bytes(2, ctypes.byref(d), T, 0)
         assert n >= prev
         prev = n
+
+
+def test_probe_stream_read_validation(lib):
+    ok = ctypes.c_void_p(FAKE)
+    bad = ctypes.c_void_p(FAKE + 8)
+    assert lib.lrkv_probe_stream_read(None, 1024, ok, 4, None) == L.LRKV_ERR_INVALID_ARG
+    assert lib.lrkv_probe_stream_read(ok, 1000, ok, 4, None) == L.LRKV_ERR_INVALID_ARG
+    assert lib.lrkv_probe_stream_read(bad, 1024, ok, 4, None) == L.LRKV_ERR_INVALID_ARG
+    assert lib.lrkv_probe_stream_read(ok, 1024, None, 4, None) == L.LRKV_ERR_INVALID_ARG
+    assert lib.lrkv_probe_stream_read(ok, 1024, ok, 0, None) == L.LRKV_ERR_INVALID_ARG

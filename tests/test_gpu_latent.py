@@ -302,3 +302,18 @@ def test_rope_gqa_full_size_sampled():
                                     1, 1, dh, th)
             err = rel_l2(got[b:b + 1, j], ref[:, 0]).max()
             assert err <= TOL, (u, b, err)
+
+
+def test_probe_stream_read_reads_every_word():
+    """The streaming-read reference reads each 32-bit word exactly once: the XOR
+    of its per-workgroup words equals the XOR of the buffer."""
+    import rank_compressed_kv_amd as R
+    say("stream-read probe")
+    rng = np.random.default_rng(7)
+    host = rng.integers(0, 2 ** 32, size=(1 << 20) + 4 * 37, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    for blocks in (1, 3, 64):
+        out = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+        R.probe_stream_read(buf, out, blocks)
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), blocks
