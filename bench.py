@@ -130,6 +130,17 @@ def measure_rows(torch, lrkv, dev, iters: int = 20) -> dict:
     out = torch.empty((Bq, U * S * GQ, R), dtype=torch.float32, device=dev)
     ms = _time(torch, lambda: lrkv.decode_attn(lrkv.MODE_ABSORBED, c.desc, qa, None, None, 0.0, out, ws, Tq), iters)
     rows["absorbed_fp16_B16_T16384"] = _row(ms, Bq * U * Tq * BYTES_PER_UNIT_TOKEN, Bq * U * Tq * 4 * S * R)
+    del c, ws
+
+    # absorbed over int4 latents (symmetric codes, one fp16 scale per 32 elements
+    # per token), same layer and batch: codes + scales are 288 B per unit-token
+    c = lrkv.LatentCache(Bq, U, S, GQ, DH, R, Tq, lrkv.FMT_INT4_G32, 0.0, device=dev)
+    for chunk in range(0, Tq, 4096):
+        c.append(torch.randn((Bq, U, 4096, R), generator=g, device=dev) * sq,
+                 torch.randn((Bq, U, 4096, R), generator=g, device=dev) * sq)
+    ws = c.workspace(lrkv.MODE_ABSORBED)
+    ms = _time(torch, lambda: lrkv.decode_attn(lrkv.MODE_ABSORBED, c.desc, qa, None, None, 0.0, out, ws, Tq), iters)
+    rows["absorbed_int4_B16_T16384"] = _row(ms, Bq * U * Tq * 2 * (R // 2 + 2 * R // 32), Bq * U * Tq * 4 * S * R)
     del c, qa, ws, out
 
     # RoPE path over Hadamard-rotated int4 latents: Llama-3-8B GQA, rank 64 per KV head
