@@ -24,12 +24,32 @@ struct AbsorbArgs {
 
 // Every wave streams its own 32-token tiles (tile w, w+4, ...) with no barrier:
 // scores on a 16x16x32 MFMA (A = key rows straight from memory, B = the absorbed
-// queries, heads padded to 16), p x H^v on a second 16x16x32 MFMA whose token
-// order follows the score layout, then the 4 wave states are merged in LDS.
+// queries, heads padded to 16), p x H^v on a second 16x16x32 MFMA, then the 4
+// wave states are merged in LDS. Row m of score M-tile mt is token
+// 8 (m / 4) + 4 mt + m % 4 of the tile, so lane group g ends up holding tokens
+// 8 g .. 8 g + 7: the value fragments are then one contiguous run of the
+// dimension-major value block (fp16: 16 bytes; int4: one 32-bit word).
+// int4 keys: lane group g reads 16-byte chunks g + 4 q of a token's codes
+// (rank 256: q = 0, 1), word w of chunk q serving K step 4 q + w; smaller ranks
+// read one word per K step. Codes decode with the exponent-bias trick (element
+// order 0, 4, 1, 5, 2, 6, 3, 7 of a word); the queries are loaded in the same
+// rank order. int4 value scales are folded into p per 32-dim group.
+template <int R>
+struct KeyMap {
+    static constexpr bool CHUNK = R >= 128;            // 16-byte chunks per lane group
+    static constexpr int NQ = R / 128;                  // chunks per lane group
+    // first rank of the 8 codes that lane group g feeds K step kk
+    __host__ __device__ static constexpr int rank0(int kk, int g) {
+        return CHUNK ? 32 * (g + 4 * (kk >> 2)) + 8 * (kk & 3) : 32 * kk + 8 * g;
+    }
+};
+
 template <int R, int NH, bool INT4>
 __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
     constexpr int KS = R / 32;
     constexpr int VM = R / 16;
+    constexpr int NG = R / 32;
+    using KM = KeyMap<R>;
     static_assert(NH <= 16, "at most 16 query heads per unit");
     __shared__ float wst[4][NH][R + 2];
 
@@ -50,25 +70,25 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
         return;
     }
 
-    // B fragments of the absorbed queries: head hn = l%16, dims 32kk + 8(l/16) + 0..7,
-    // scaled by qscale * 2^e per head (max |q'| in [2^14, 2^15)).
+    // B fragments of the absorbed queries: head hn = l%16, the 8 ranks lane group
+    // g feeds K step kk, scaled by qscale * 2^e per head (max |q'| in [2^14, 2^15)).
     const int hn = l & 15, g = l >> 4;
     half8 qf[KS];
     float inv = 1.0f;
     {
         float qv[KS][8];
         float mx = 0.0f;
-        // unconditional 16-byte loads (padding heads read head NH - 1, then zero)
-        const float* qrow = p.q + ((long)b * Hq + j0 + (hn < NH ? hn : NH - 1)) * R + 8 * g;
+        const float* qrow = p.q + ((long)b * Hq + j0 + (hn < NH ? hn : NH - 1)) * R;
         const float qs = hn < NH ? p.qscale : 0.0f;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * kk);
-            const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * kk + 4);
+            const int r0 = INT4 ? KM::rank0(kk, g) : 32 * kk + 8 * g;
+            const float4 x0 = *reinterpret_cast<const float4*>(qrow + r0);
+            const float4 x1 = *reinterpret_cast<const float4*>(qrow + r0 + 4);
             const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qv[kk][e] = xs[e] * qs;
+                qv[kk][e] = xs[INT4 ? code_pos_inv(e) : e] * qs;
                 mx = fmaxf(mx, fabsf(qv[kk][e]));
             }
         }
@@ -86,6 +106,9 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
     floatx4 acc[VM];
 #pragma unroll
     for (int v = 0; v < VM; ++v) acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic = 0x64006400u;
+    // token of row hn of score M-tile mt
+    const int trow = 8 * (hn >> 2) + (hn & 3);
 
     const int n_tiles = (t_end - t_begin + 31) / 32;
     for (int it = w; it < n_tiles; it += 4) {
@@ -93,43 +116,56 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
         const bool tail = t0 + 32 > t_end;
         const long blk_base = bu * (p.cap / kTile) + t0 / kTile;
         // every load of the tile is issued before the first MFMA: key rows
-        // t0 + 16 mt + hn (clamped to the last valid token; their scores are
-        // masked), value dims 16 v + hn at tokens {4g..4g+3, 16+4g..16+4g+3}
+        // (clamped to the last valid token; their scores are masked), value dims
+        // 16 v + hn at tokens 8 g .. 8 g + 7
         half8 ka[2][KS], va[VM];
-        uint32_t kcode[2][KS], vlo[VM], vhi[VM];
-        half_t ksc[2][KS];
-        half4 vslo[VM], vshi[VM];
+        uint32_t kw[2][KS], vc[VM];
+        uint32_t ksc[2][KS];
+        half8 vs[NG];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const long row = bu * p.cap + min(t0 + 16 * mt + hn, t_end - 1);
+            const long row = bu * p.cap + min(t0 + trow + 4 * mt, t_end - 1);
+            if constexpr (!INT4) {
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                if constexpr (!INT4) {
+                for (int kk = 0; kk < KS; ++kk)
                     ka[mt][kk] = *reinterpret_cast<const half8*>((const half_t*)p.hk + row * R + 32 * kk + 8 * g);
-                } else {
-                    kcode[mt][kk] = *reinterpret_cast<const uint32_t*>((const uint8_t*)p.hk + row * (R / 2) + 16 * kk + 4 * g);
-                    ksc[mt][kk] = p.sk[row * (R / 32) + kk];
+            } else if constexpr (KM::CHUNK) {
+                const uint8_t* kr = (const uint8_t*)p.hk + row * (R / 2);
+                const uint16_t* sr = reinterpret_cast<const uint16_t*>(p.sk) + row * (R / 32);
+#pragma unroll
+                for (int q = 0; q < KM::NQ; ++q) {
+                    const uint4 c4 = *reinterpret_cast<const uint4*>(kr + 16 * (g + 4 * q));
+                    kw[mt][4 * q + 0] = c4.x;
+                    kw[mt][4 * q + 1] = c4.y;
+                    kw[mt][4 * q + 2] = c4.z;
+                    kw[mt][4 * q + 3] = c4.w;
+                    const uint32_t sc = sr[g + 4 * q];
+#pragma unroll
+                    for (int wd = 0; wd < 4; ++wd) ksc[mt][4 * q + wd] = sc;
+                }
+            } else {
+                const uint16_t* sr = reinterpret_cast<const uint16_t*>(p.sk) + row * (R / 32);
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    kw[mt][kk] = *reinterpret_cast<const uint32_t*>((const uint8_t*)p.hk + row * (R / 2) + 16 * kk + 4 * g);
+                    ksc[mt][kk] = sr[kk];
                 }
             }
         }
 #pragma unroll
         for (int v = 0; v < VM; ++v) {
             const int dim = 16 * v + hn;
-            if constexpr (!INT4) {
-                const half_t* src = (const half_t*)p.hv + (blk_base * R + dim) * kTile;
-                const half4 lo = *reinterpret_cast<const half4*>(src + 4 * g);
-                const half4 hi = *reinterpret_cast<const half4*>(src + 16 + 4 * g);
-                va[v] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-                const uint8_t* src = (const uint8_t*)p.hv + (blk_base * R + dim) * (kTile / 2);
-                vlo[v] = *reinterpret_cast<const uint16_t*>(src + 2 * g);
-                vhi[v] = *reinterpret_cast<const uint16_t*>(src + 8 + 2 * g);
-                const half_t* ss = p.sv + (blk_base * (R / 32) + dim / 32) * kTile;
-                vslo[v] = *reinterpret_cast<const half4*>(ss + 4 * g);
-                vshi[v] = *reinterpret_cast<const half4*>(ss + 16 + 4 * g);
-            }
+            if constexpr (!INT4)
+                va[v] = *reinterpret_cast<const half8*>((const half_t*)p.hv + (blk_base * R + dim) * kTile + 8 * g);
+            else
+                vc[v] = *reinterpret_cast<const uint32_t*>((const uint8_t*)p.hv + (blk_base * R + dim) * (kTile / 2) + 4 * g);
         }
-        // scores: two 16-token M-tiles; lane holds tokens 16mt + 4g + e for head hn
+        if constexpr (INT4) {
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr)
+                vs[gr] = *reinterpret_cast<const half8*>(p.sv + (blk_base * NG + gr) * kTile + 8 * g);
+        }
+        // scores: lane holds head hn at tokens 8 g + 4 mt + e
         floatx4 sc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -137,69 +173,83 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 half8 a;
-                if constexpr (!INT4) {
-                    a = ka[mt][kk];
-                } else {
-                    const float s = (float)ksc[mt][kk];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a[e] = (half_t)((float)nibble(kcode[mt][kk], e) * s);
-                }
+                if constexpr (!INT4) a = ka[mt][kk];
+                else a = dequant_keys(kw[mt][kk], ksc[mt][kk], magic);
                 sc[mt] = mfma16(a, qf[kk], sc[mt]);
             }
         }
         float s8[8];
         float mt_loc = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = t0 + 16 * mt + 4 * g + e;
-                const float v = t < t_end ? sc[mt][e] * inv : -INFINITY;
-                s8[4 * mt + e] = v;
-                mt_loc = fmaxf(mt_loc, v);
-            }
+        for (int k = 0; k < 8; ++k) {
+            const float v = t0 + 8 * g + k < t_end ? sc[k >> 2][k & 3] * inv : -INFINITY;
+            s8[k] = v;
+            mt_loc = fmaxf(mt_loc, v);
+        }
         mt_loc = fmaxf(mt_loc, __shfl_xor(mt_loc, 16, kWave));
         mt_loc = fmaxf(mt_loc, __shfl_xor(mt_loc, 32, kWave));
         const float mn = fmaxf(m_run, mt_loc);
-        const float alpha = exp2f(m_run - mn);
-        half8 pf;
+        // the accumulators are rescaled only when some head's running max moved
+        const bool moved = __builtin_amdgcn_ballot_w64(mn > m_run) != 0;
+        const float alpha = moved ? exp2f(m_run - mn) : 1.0f;
+        float pr[8];
         float psum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pv = exp2f(s8[e] - mn);
-            psum += pv;
-            pf[e] = (half_t)pv;
+        for (int k = 0; k < 8; ++k) {
+            pr[k] = hn < NH ? exp2f(s8[k] - mn) : 0.0f;
+            psum += pr[k];
         }
         psum += __shfl_xor(psum, 16, kWave);
         psum += __shfl_xor(psum, 32, kWave);
         l_run = fmaf(l_run, alpha, psum);
         m_run = mn;
-        if (hn >= NH) pf = half8{};
-        // values: A = V^T [16 dims][tokens {4g..4g+3, 16+4g..16+4g+3}]
-        if constexpr (INT4) {
+        if (moved) {
 #pragma unroll
-            for (int v = 0; v < VM; ++v)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    va[v][e] = (half_t)((float)nibble(vlo[v], e) * (float)vslo[v][e]);
-                    va[v][4 + e] = (half_t)((float)nibble(vhi[v], e) * (float)vshi[v][e]);
-                }
+            for (int v = 0; v < VM; ++v) acc[v] *= alpha;
         }
-        if (tail) {
-            // tokens past t_end: zero (their p is zero; the memory may hold anything)
+        if constexpr (!INT4) {
+            half8 pf;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = t0 + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-                if (t >= t_end) {
+            for (int k = 0; k < 8; ++k) pf[k] = (half_t)pr[k];
+            if (tail) {
+                // tokens past t_end: zero (their p is zero; the memory may hold anything)
 #pragma unroll
-                    for (int v = 0; v < VM; ++v) va[v][e] = (half_t)0.0f;
-                }
+                for (int k = 0; k < 8; ++k)
+                    if (t0 + 8 * g + k >= t_end) {
+#pragma unroll
+                        for (int v = 0; v < VM; ++v) va[v][k] = (half_t)0.0f;
+                    }
             }
-        }
 #pragma unroll
-        for (int v = 0; v < VM; ++v) {
-            acc[v] *= alpha;
-            acc[v] = mfma16(va[v], pf, acc[v]);
+            for (int v = 0; v < VM; ++v) acc[v] = mfma16(va[v], pf, acc[v]);
+        } else {
+            // p in the code order (tokens 0, 4, 1, 5, 2, 6, 3, 7 of the group) times the
+            // token's value scale of each 32-dim group; past t_end both are zeroed
+            // (the scale there may hold anything)
+            half2_t pk[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pk[i] = pack2(pr[i], pr[4 + i]);
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr) {
+                const uint4 sw = __builtin_bit_cast(uint4, vs[gr]);
+                half2_t sp[4] = {__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(sw.z, sw.x, 0x05040100u)),
+                                 __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(sw.z, sw.x, 0x07060302u)),
+                                 __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(sw.w, sw.y, 0x05040100u)),
+                                 __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(sw.w, sw.y, 0x07060302u))};
+                half2_t pp[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pp[i] = pk[i] * sp[i];
+                if (tail) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (t0 + 8 * g + i >= t_end) pp[i].x = (half_t)0.0f;
+                        if (t0 + 8 * g + 4 + i >= t_end) pp[i].y = (half_t)0.0f;
+                    }
+                }
+                const half8 pf = as_half8(pp);
+#pragma unroll
+                for (int v = 2 * gr; v < 2 * gr + 2; ++v) acc[v] = mfma16(value_codes(vc[v], magic), pf, acc[v]);
+            }
         }
     }
 

@@ -155,6 +155,54 @@ __device__ __forceinline__ half8 load_vfrag(const void* hv, const half_t* sv, lo
     return a;
 }
 
+// ---------------------------------------------------------------- int4 codes
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2_t pack2(float a, float b) { return half2_t{(half_t)a, (half_t)b}; }
+
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+    return r;
+}
+
+// The 8 two's complement nibbles of a word of codes (element k at bits 4k) as
+// exact fp16 values, in the order k = 0, 4, 1, 5, 2, 6, 3, 7: after flipping
+// the sign bits (code + 8 in 0..15), the nibble pair (k, k + 4) of each byte
+// position is masked into the mantissas of 0x6400 = 1024 (k even: 1024 + c + 8;
+// k odd, 4 bits up: 1024 + 16 (c + 8)); both are exact, as are the offsets.
+__device__ __forceinline__ void unpack_codes(uint32_t w, uint32_t magic, half2_t* r) {
+    const uint32_t x = w ^ 0x88888888u, y = x >> 8;
+    const half2_t lo_off = {-1032.0f16, -1032.0f16};
+    const half2_t hi_mul = {0.0625f16, 0.0625f16}, hi_off = {-72.0f16, -72.0f16};
+    r[0] = __builtin_bit_cast(half2_t, and_or(x, 0x000F000Fu, magic)) + lo_off;
+    r[1] = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(x, 0x00F000F0u, magic)), hi_mul, hi_off);
+    r[2] = __builtin_bit_cast(half2_t, and_or(y, 0x000F000Fu, magic)) + lo_off;
+    r[3] = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(y, 0x00F000F0u, magic)), hi_mul, hi_off);
+}
+// Source nibble of element e (0..7) of an unpacked word: 0, 4, 1, 5, 2, 6, 3, 7.
+__host__ __device__ constexpr int code_pos_inv(int e) { return (e & 1) ? 4 + (e >> 1) : e >> 1; }
+__device__ __forceinline__ half8 as_half8(const half2_t* r) {
+    return __builtin_bit_cast(half8, uint4{__builtin_bit_cast(uint32_t, r[0]), __builtin_bit_cast(uint32_t, r[1]),
+                                           __builtin_bit_cast(uint32_t, r[2]), __builtin_bit_cast(uint32_t, r[3])});
+}
+// Keys: codes x the token's fp16 scale (bits in the low half of sc; one
+// rounding, as code * scale in fp16).
+__device__ __forceinline__ half8 dequant_keys(uint32_t w, uint32_t sc, uint32_t magic) {
+    half2_t r[4];
+    unpack_codes(w, magic, r);
+    const half2_t s2 = __builtin_bit_cast(half2_t, sc * 0x00010001u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] *= s2;
+    return as_half8(r);
+}
+// Values: the codes alone (the per-token scale is folded into p).
+__device__ __forceinline__ half8 value_codes(uint32_t w, uint32_t magic) {
+    half2_t r[4];
+    unpack_codes(w, magic, r);
+    return as_half8(r);
+}
+
 // ---------------------------------------------------------------- RoPE angles
 // Tables written by the query-preparation step (fp64 angles, fp32 values):
 //   step[f]      = (cos, sin)(32 theta_f)                   rotation by one tile

@@ -233,12 +233,15 @@ def test_rope_off_equals_absorbed():
 
 # ----------------------------------------------------------------------------- absorbed path
 
-@pytest.mark.parametrize("fmt_name,B,T,cap", [("fp16", 3, 700, 704), ("fp16", 2, 4096, 4096), ("int4", 2, 999, 1024)])
-def test_absorbed_parity(fmt_name, B, T, cap):
+@pytest.mark.parametrize("fmt_name,B,T,cap,r,s", [("fp16", 3, 700, 704, 256, 4), ("fp16", 2, 4096, 4096, 256, 4),
+                                                  ("int4", 2, 999, 1024, 256, 4), ("int4", 3, 2000, 2048, 128, 4),
+                                                  ("int4", 2, 515, 544, 64, 2), ("int4", 1, 77, 96, 32, 2),
+                                                  ("fp16", 2, 333, 352, 64, 2)])
+def test_absorbed_parity(fmt_name, B, T, cap, r, s):
     R = _R()
     fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
-    say(f"absorbed parity: {fmt_name} B={B} T={T}")
-    U, s, r, dh = 8, 4, 256, 128
+    say(f"absorbed parity: {fmt_name} B={B} T={T} r={r} heads/unit={s}")
+    U, dh = 8, 128
     lay = synth.latent_layer(31, B, U, T, r, s * dh, 96.0)
     qa = synth.queries(32, B, U * s, r, 3.0)
     cache = R.LatentCache(B, U, s, 1, dh, r, cap, fmt, 0.0)
