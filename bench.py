@@ -143,6 +143,27 @@ def measure_rows(torch, lrkv, dev, iters: int = 20) -> dict:
     rows["absorbed_int4_B16_T16384"] = _row(ms, Bq * U * Tq * 2 * (R // 2 + 2 * R // 32), Bq * U * Tq * 4 * S * R)
     del c, qa, ws, out
 
+    # the projections on either side of the path (Llama-2-7B layer): latents of K and V
+    # for a new token of every sequence (one call, 16 units of rank 256, d 4096) and
+    # the output projection with B^v fused into W^o (32 heads x 256 -> 4096); fp16
+    # weights streamed once per call
+    g.manual_seed(6)
+    DM = U * S * DH
+    a_t = (torch.randn((2 * U * R, DM), generator=g, device=dev) / DM ** 0.5).half()
+    w_t = (torch.randn((DM, U * S * R), generator=g, device=dev) / (U * S * R) ** 0.5).half()
+    for nb in (1, 16):
+        x = torch.randn((nb, DM), generator=g, device=dev)
+        o = torch.randn((nb, U * S, R), generator=g, device=dev)
+        h = torch.empty((nb, 2 * U, R), dtype=torch.float32, device=dev)
+        y = torch.empty((nb, DM), dtype=torch.float32, device=dev)
+        wsl = torch.empty(lrkv.project_workspace_bytes(nb, 2 * U * R, DM), dtype=torch.uint8, device=dev)
+        wso = torch.empty(lrkv.project_workspace_bytes(nb, DM, U * S * R), dtype=torch.uint8, device=dev)
+        ms = _time(torch, lambda: lrkv.latent_project(x, a_t, 2 * U, R, h, wsl), iters)
+        rows[f"latent_project_kv_B{nb}"] = _row(ms, a_t.numel() * 2, 2 * nb * a_t.numel())
+        ms = _time(torch, lambda: lrkv.output_project(o, w_t, y, wso), iters)
+        rows[f"output_project_B{nb}"] = _row(ms, w_t.numel() * 2, 2 * nb * w_t.numel())
+    del a_t, w_t, x, o, h, y, wsl, wso
+
     # RoPE path over Hadamard-rotated int4 latents: Llama-3-8B GQA, rank 64 per KV head
     g.manual_seed(4)
     B4, T4, H4, G4, R4 = 4, 65536, 8, 4, 64

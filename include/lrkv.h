@@ -276,6 +276,35 @@ int32_t lrkv_paged_plan(const lrkv_paged_cache *cache, const int32_t *host_lens,
                         int32_t *out, int32_t max_out);
 
 /*
+ * The projections on either side of the decode path (Palu digest, Method
+ * details: a token is cached as its latents h = x A, and the value
+ * up-projection B^v is fused offline into W^o, so the layer output is
+ * y = sum_j o_j (B^v_j W^o_j) with o_j the latent-space output of head j).
+ * Both compute C[M][N] = X[M][K] W^T[N][K]^T with fp32 X and C and fp16
+ * weights W^T stored with K contiguous (row-major [N][K]); all pointers are
+ * device memory, 16-byte aligned; K must be a multiple of 32 and N of 16
+ * (LRKV_ERR_UNSUPPORTED otherwise). The partial sums of the K split go to the
+ * caller's `workspace` (device, at least lrkv_project_workspace_bytes(M, N, K)
+ * bytes, else LRKV_ERR_WORKSPACE); their final sum is in a fixed order, so a
+ * call is deterministic. Enqueued on `stream`; nothing is allocated.
+ *
+ * lrkv_latent_project: x [n_tok][d_model] (one token per row), a_t
+ *   [units * rank][d_model] = (A_u)^T of each unit stacked, h [n_tok][units][rank]
+ *   (for one new token per sequence this is lrkv_append_latent's new_k / new_v
+ *   layout). M = n_tok, K = d_model, N = units * rank.
+ * lrkv_output_project: o [batch][q_heads][rank] (lrkv_decode_attn's output in
+ *   the Palu modes), w_t [d_model][q_heads * rank] with column j * rank + i =
+ *   row i of head j's fused B^v_j W^o_j, y [batch][d_model].
+ *   M = batch, K = q_heads * rank, N = d_model.
+ * lrkv_project_workspace_bytes: 0 for invalid sizes.
+ */
+size_t lrkv_project_workspace_bytes(int32_t m, int32_t n, int32_t k);
+int32_t lrkv_latent_project(const float *x, int32_t n_tok, int32_t d_model, const void *a_t, int32_t units,
+                            int32_t rank, float *h, void *workspace, size_t ws_bytes, void *stream);
+int32_t lrkv_output_project(const float *o, int32_t batch, int32_t q_heads, int32_t rank, const void *w_t,
+                            int32_t d_model, float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Measurement aid, not part of the decode path: reads `bytes` (a multiple of
  * 16) of device memory `buf` once with a streaming kernel of `blocks`
  * workgroups (1..65535) and writes one word per workgroup to device `out`

@@ -77,6 +77,16 @@ def hadamard_fold(A: np.ndarray, B: np.ndarray, R: np.ndarray) -> tuple[np.ndarr
     return A @ R, R.T @ B
 
 
+def latent_project(x: np.ndarray, A_units: np.ndarray) -> np.ndarray:
+    """Latents of every unit for tokens x [n][d]: h[t][u] = x_t A_u, A_units [U][d][r] -> [n][U][r].
+
+    Palu digest, Method details: the cache stores h = x A in place of keys and values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    A = np.asarray(A_units, dtype=np.float64)
+    return np.stack([x @ A[u] for u in range(A.shape[0])], axis=1)
+
+
 def fuse_v_into_wo(Bv_head: np.ndarray, Wo_head: np.ndarray) -> np.ndarray:
     """B^v_i W^o_i (r x d): value reconstruction absorbed into the output projection.
 

@@ -28,7 +28,8 @@ BLOCK = 32
 EXPORTS = (
     "lrkv_status_string", "lrkv_version", "lrkv_decode_workspace_bytes", "lrkv_append_latent",
     "lrkv_decode_attn", "lrkv_decode_prepare", "lrkv_decode_partials", "lrkv_merge_partials",
-    "lrkv_factor_page", "lrkv_paged_plan", "lrkv_probe_stream_read",
+    "lrkv_factor_page", "lrkv_paged_plan", "lrkv_project_workspace_bytes", "lrkv_latent_project",
+    "lrkv_output_project", "lrkv_probe_stream_read",
 )
 
 c_i32 = ctypes.c_int32
@@ -94,6 +95,12 @@ def lib() -> ctypes.CDLL:
         L.lrkv_factor_page.restype = c_i32
         L.lrkv_paged_plan.argtypes = [ctypes.POINTER(PagedCacheDesc), c_vp, c_i32, c_vp, c_i32]
         L.lrkv_paged_plan.restype = c_i32
+        L.lrkv_project_workspace_bytes.argtypes = [c_i32, c_i32, c_i32]
+        L.lrkv_project_workspace_bytes.restype = ctypes.c_size_t
+        L.lrkv_latent_project.argtypes = [c_vp, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp, ctypes.c_size_t, c_vp]
+        L.lrkv_latent_project.restype = c_i32
+        L.lrkv_output_project.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, ctypes.c_size_t, c_vp]
+        L.lrkv_output_project.restype = c_i32
         L.lrkv_probe_stream_read.argtypes = [c_vp, ctypes.c_size_t, c_vp, c_i32, c_vp]
         L.lrkv_probe_stream_read.restype = c_i32
         _lib = L

@@ -18,7 +18,8 @@ from ._lib import (BLOCK, FMT_FP16, FMT_INT4_G32, MODE_ABSORBED, MODE_HYBRID_PAG
 
 __all__ = [
     "decode_workspace_bytes", "append_latent", "decode_attn", "decode_prepare", "decode_partials",
-    "merge_partials", "factor_page", "paged_plan", "probe_stream_read",
+    "merge_partials", "factor_page", "paged_plan", "project_workspace_bytes", "latent_project",
+    "output_project", "probe_stream_read",
     "LatentCache", "PagedCache", "LrkvError",
     "MODE_ROPE_RECON", "MODE_ABSORBED", "MODE_HYBRID_PAGED", "FMT_FP16", "FMT_INT4_G32",
 ]
@@ -87,6 +88,50 @@ def factor_page(desc, pages, n_pages: int, src_k=None, src_v=None, src_len: int 
                 max_sweeps: int = 0, stream=None) -> None:
     L.check(L.lib().lrkv_factor_page(ctypes.byref(desc), _p(pages), n_pages, _p(src_k), _p(src_v),
                                      src_len, max_sweeps, _stream(stream)), "lrkv_factor_page")
+
+
+def project_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(L.lib().lrkv_project_workspace_bytes(m, n, k))
+
+
+def _proj_ws(m, n, k, workspace, device):
+    need = project_workspace_bytes(m, n, k)
+    if need == 0:
+        raise LrkvError(L.LRKV_ERR_INVALID_ARG, "lrkv_project_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def latent_project(x, a_t, units: int, rank: int, h=None, workspace=None, stream=None):
+    """h = x A for every unit: x float32 [n_tok][d_model], a_t float16
+    [units * rank][d_model] -> h float32 [n_tok][units][rank]."""
+    n_tok, d_model = x.shape
+    _need(x, torch.float32, (n_tok, d_model), "x")
+    _need(a_t, torch.float16, (units * rank, d_model), "a_t")
+    if h is None:
+        h = torch.empty((n_tok, units, rank), dtype=torch.float32, device=x.device)
+    _need(h, torch.float32, (n_tok, units, rank), "h")
+    workspace = _proj_ws(n_tok, units * rank, d_model, workspace, x.device)
+    L.check(L.lib().lrkv_latent_project(_p(x), n_tok, d_model, _p(a_t), units, rank, _p(h), _p(workspace),
+                                        _ws(workspace), _stream(stream)), "lrkv_latent_project")
+    return h
+
+
+def output_project(o, w_t, y=None, workspace=None, stream=None):
+    """y = sum_j o_j (B^v_j W^o_j): o float32 [batch][q_heads][rank], w_t float16
+    [d_model][q_heads * rank] -> y float32 [batch][d_model]."""
+    batch, q_heads, rank = o.shape
+    d_model = w_t.shape[0]
+    _need(o, torch.float32, (batch, q_heads, rank), "o")
+    _need(w_t, torch.float16, (d_model, q_heads * rank), "w_t")
+    if y is None:
+        y = torch.empty((batch, d_model), dtype=torch.float32, device=o.device)
+    _need(y, torch.float32, (batch, d_model), "y")
+    workspace = _proj_ws(batch, d_model, q_heads * rank, workspace, o.device)
+    L.check(L.lib().lrkv_output_project(_p(o), batch, q_heads, rank, _p(w_t), d_model, _p(y), _p(workspace),
+                                        _ws(workspace), _stream(stream)), "lrkv_output_project")
+    return y
 
 
 def probe_stream_read(buf, out, blocks: int = 4096, stream=None) -> None:

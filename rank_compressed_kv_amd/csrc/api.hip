@@ -307,6 +307,41 @@ int32_t lrkv_paged_plan(const lrkv_paged_cache* c, const int32_t* host_lens, int
     return count > 0x7fffffff ? LRKV_ERR_INVALID_ARG : (int32_t)count;
 }
 
+static int32_t check_skinny(const void* X, const void* Wt, const void* C, int M, int N, int K) {
+    if (!X || !Wt || !C || M < 1 || N < 1 || K < 1) return LRKV_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(Wt)) return LRKV_ERR_INVALID_ARG;
+    if ((K % 32) || (N % 16)) return LRKV_ERR_UNSUPPORTED;
+    if ((long)M * N >= (1L << 31) || (long)N * K >= (1L << 40)) return LRKV_ERR_INVALID_ARG;
+    return LRKV_OK;
+}
+
+size_t lrkv_project_workspace_bytes(int32_t m, int32_t n, int32_t k) {
+    if (m < 1 || n < 1 || k < 1 || (k % 32) || (n % 16) || (long)m * n >= (1L << 31)) return 0;
+    return skinny_plan(m, n, k).ws_bytes;
+}
+
+int32_t lrkv_latent_project(const float* x, int32_t n_tok, int32_t d_model, const void* a_t, int32_t units,
+                            int32_t rank, float* h, void* workspace, size_t ws_bytes, void* stream) {
+    if (units < 1 || rank < 1 || (long)units * rank >= (1L << 30)) return LRKV_ERR_INVALID_ARG;
+    const int N = units * rank;
+    int32_t rc = check_skinny(x, a_t, h, n_tok, N, d_model);
+    if (rc != LRKV_OK) return rc;
+    const SkinnyPlan p = skinny_plan(n_tok, N, d_model);
+    if (!workspace || ws_bytes < p.ws_bytes) return LRKV_ERR_WORKSPACE;
+    return launch_skinny(x, (const half_t*)a_t, h, n_tok, N, d_model, workspace, p, (hipStream_t)stream);
+}
+
+int32_t lrkv_output_project(const float* o, int32_t batch, int32_t q_heads, int32_t rank, const void* w_t,
+                            int32_t d_model, float* y, void* workspace, size_t ws_bytes, void* stream) {
+    if (q_heads < 1 || rank < 1 || (long)q_heads * rank >= (1L << 30)) return LRKV_ERR_INVALID_ARG;
+    const int K = q_heads * rank;
+    int32_t rc = check_skinny(o, w_t, y, batch, d_model, K);
+    if (rc != LRKV_OK) return rc;
+    const SkinnyPlan p = skinny_plan(batch, d_model, K);
+    if (!workspace || ws_bytes < p.ws_bytes) return LRKV_ERR_WORKSPACE;
+    return launch_skinny(o, (const half_t*)w_t, y, batch, d_model, K, workspace, p, (hipStream_t)stream);
+}
+
 int32_t lrkv_probe_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* stream) {
     if (!buf || !out || bytes == 0 || (bytes % 16) || (((uintptr_t)buf) & 15) || blocks < 1 || blocks > 65535)
         return LRKV_ERR_INVALID_ARG;

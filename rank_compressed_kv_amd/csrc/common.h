@@ -105,6 +105,15 @@ struct PagedWorkspace {
 PagedWorkspace paged_workspace(const lrkv_paged_cache* c, int host_max_len, int n_split);
 int32_t launch_decode_hybrid(int phases, const lrkv_paged_cache* c, const float* q, float sm_scale,
                              float* out, void* ws, const PagedWorkspace& w, hipStream_t st);
+// Weight-stream GEMM C[M][N] = X[M][K] W^T[N][K]^T (fp32 X and C, fp16 W):
+// K split into k_split ranges of kchunk, partial sums in the workspace.
+struct SkinnyPlan {
+    int kchunk, k_split;
+    size_t ws_bytes;
+};
+SkinnyPlan skinny_plan(int M, int N, int K);
+int32_t launch_skinny(const float* X, const half_t* Wt, float* C, int M, int N, int K, void* ws,
+                      const SkinnyPlan& p, hipStream_t st);
 int32_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t st);
 int32_t launch_factor_page(const lrkv_paged_cache* c, const int32_t* pages, int n_pages,
                            const half_t* src_k, const half_t* src_v, int src_len, int max_sweeps,

@@ -177,3 +177,24 @@ def test_probe_stream_read_validation(lib):
     assert lib.lrkv_probe_stream_read(bad, 1024, ok, 4, None) == L.LRKV_ERR_INVALID_ARG
     assert lib.lrkv_probe_stream_read(ok, 1024, None, 4, None) == L.LRKV_ERR_INVALID_ARG
     assert lib.lrkv_probe_stream_read(ok, 1024, ok, 0, None) == L.LRKV_ERR_INVALID_ARG
+
+
+def test_projection_validation(lib):
+    ok = ctypes.c_void_p(FAKE)
+    need = lib.lrkv_project_workspace_bytes(4, 4096, 8192)
+    assert need >= 4 * 4096 * 4
+    assert lib.lrkv_project_workspace_bytes(4, 4096, 8190) == 0       # K not a multiple of 32
+    assert lib.lrkv_project_workspace_bytes(4, 4100, 8192) == 0       # N not a multiple of 16
+    assert lib.lrkv_project_workspace_bytes(0, 4096, 8192) == 0
+    # latent projection: x [n][d], a_t [U r][d], h [n][U][r]
+    assert lib.lrkv_latent_project(None, 4, 4096, ok, 8, 256, ok, ok, 1 << 30, None) == L.LRKV_ERR_INVALID_ARG
+    assert lib.lrkv_latent_project(ok, 4, 4096, ok, 1, 250, ok, ok, 1 << 30, None) == L.LRKV_ERR_UNSUPPORTED
+    assert lib.lrkv_latent_project(ok, 4, 4001, ok, 8, 256, ok, ok, 1 << 30, None) == L.LRKV_ERR_UNSUPPORTED
+    ws = lib.lrkv_project_workspace_bytes(4, 8 * 256, 4096)
+    assert lib.lrkv_latent_project(ok, 4, 4096, ok, 8, 256, ok, ok, ws - 4, None) == L.LRKV_ERR_WORKSPACE
+    assert lib.lrkv_latent_project(ok, 4, 4096, ok, 8, 256, ok, None, ws, None) == L.LRKV_ERR_WORKSPACE
+    # output projection: o [B][Hq][r], w_t [d][Hq r], y [B][d]
+    assert lib.lrkv_output_project(ok, 0, 32, 256, ok, 4096, ok, ok, need, None) == L.LRKV_ERR_INVALID_ARG
+    assert lib.lrkv_output_project(ok, 4, 32, 256, None, 4096, ok, ok, need, None) == L.LRKV_ERR_INVALID_ARG
+    assert lib.lrkv_output_project(ok, 4, 32, 256, ok, 4095, ok, ok, need, None) == L.LRKV_ERR_UNSUPPORTED
+    assert lib.lrkv_output_project(ok, 4, 32, 256, ok, 4096, ok, ok, need - 4, None) == L.LRKV_ERR_WORKSPACE

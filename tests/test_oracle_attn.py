@@ -137,3 +137,19 @@ def test_stored_formats():
     assert np.isinf(attn.stored_fp16(h)[0, 1])
     x = np.linspace(-3, 3, 64, dtype=np.float32)[None]
     assert np.abs(attn.stored_int4(x) - x).max() <= 3 / 7 / 2 + 1e-3
+
+
+def test_layer_output_fused_equals_unfused():
+    """sum_j o_j (B^v_j W^o_j) = sum_j (p_j H^v B^v_j) W^o_j: the fused output projection
+    the GPU path uses gives the unfused layer output (Palu digest, Method details)."""
+    rng = np.random.default_rng(8)
+    Hq, T, r, dh, d = 4, 9, 6, 5, 7
+    Hv = rng.standard_normal((T, r))
+    ps = [rng.dirichlet(np.ones(T)) for _ in range(Hq)]
+    Bv = [rng.standard_normal((r, dh)) for _ in range(Hq)]
+    Wo = [rng.standard_normal((dh, d)) for _ in range(Hq)]
+    o = np.stack([p @ Hv for p in ps])
+    fused = np.stack([prep.fuse_v_into_wo(b, w) for b, w in zip(Bv, Wo)])
+    got = attn.layer_output_fused(o, fused)
+    want = attn.layer_output_unfused(ps, [Hv] * Hq, Bv, Wo)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)

@@ -152,3 +152,24 @@ def test_key_fusion_identity(tiny):
     rhs = (xt @ prep.fuse_k_into_wq(Wq, Bj)) @ Hk.T
     np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-13)
     assert prep.fuse_k_into_wq(Wq, Bj).shape == (256, 32)
+
+
+def test_latent_project_full_rank_reconstructs_projection(tiny):
+    """h = x A per unit; at full rank h_u B_u = x W_u, which fixes the orientation
+    (row vectors, A on the right) and the unit order (Palu digest, Method details)."""
+    As, Bs = prep.glrd_factor(tiny["W_k"], 128)
+    h = prep.latent_project(tiny["x"], As)
+    assert h.shape == (tiny["x"].shape[0], len(tiny["W_k"]), 128)
+    for u, W in enumerate(tiny["W_k"]):
+        np.testing.assert_allclose(h[:, u] @ Bs[u], tiny["x"] @ W, rtol=1e-9, atol=1e-11)
+
+
+def test_latent_project_brute_force():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3, 5))
+    A = rng.standard_normal((2, 5, 4))
+    h = prep.latent_project(x, A)
+    for t in range(3):
+        for u in range(2):
+            for i in range(4):
+                assert abs(h[t, u, i] - sum(x[t, k] * A[u, k, i] for k in range(5))) < 1e-12
