@@ -448,7 +448,11 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
             tk.read_keys(ring + rd * kSlotBytes, c, g);
             tv.read_values(ring + pv * kSlotBytes, c, g);
             Tile::issue(rs, i + kDepth < n_tiles ? blk0 + i + kDepth : -1, ring + wr * kSlotBytes, l);
+            // the MFMA-heavy phase issues at raised priority, so that the other
+            // wave on this SIMD fills its gaps with vector work
+            __builtin_amdgcn_s_setprio(2);
             scores(tk, i & 1, sc);
+            __builtin_amdgcn_s_setprio(0);
             rotate_queries((i + 1) & 1);
             softmax_values(tv, sp, t_begin + kTile * (i - 1), Flag<false>{});
             sp[0] = sc[0];
