@@ -215,6 +215,22 @@ def measure_rows(torch, lrkv, dev, iters: int = 20) -> dict:
     rows["factor_pages_decode_batch"] = {"matrices": 2 * int(step_pages.shape[0]),
                                          "us_median": round(float(np.median(ms)) * 1e3, 2)}
     rows["factor_pages_prefill_batch"] = {"matrices": 2 * n_fac, "us": round(prefill_ms * 1e3, 1)}
+    del pc, ws
+
+    # the same cache with int4 page factors (one fp16 scale per 32 stored elements):
+    # codes + scales are (P r + r d) (1/2 + 2/32) bytes per factor pair
+    pc4 = lrkv.PagedCache(B5, H5, G5, DH, P5, 1, 4, RK, RK, T5 // P5 + 8, device=dev,
+                          factor_fmt=lrkv.FMT_INT4_G32)
+    lrkv.factor_page(pc4.desc, pages, n_fac, k5, v5, T5, 0)
+    lrkv.append_latent(lrkv.MODE_HYBRID_PAGED, pc4.desc, k5, v5, T5, 0)
+    pc4.host_lens += T5
+    torch.cuda.synchronize()
+    ws = pc4.workspace()
+    per_side = (P5 * RK + RK * DH) // 2 + (P5 * RK + RK * DH) // 32 * 2
+    by4 = B5 * H5 * (n_factored * 2 * per_side + n_dense * 2 * P5 * DH * 2)
+    ms = _time(torch, lambda: pc4.decode(q5, out=out, workspace=ws), iters)
+    rows["hybrid_paged_int4_B8_T32768"] = _row(ms, by4)
+    del pc4, ws, k5, v5
     return rows
 
 

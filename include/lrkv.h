@@ -120,6 +120,16 @@ typedef struct lrkv_latent_cache {
  *   rv          [batch][kv_heads][max_pages][head_dim][rank_v]           half  R_V^T
  *   page_table  [batch][kv_heads][max_pages]                             int32
  *
+ * factor_fmt LRKV_FMT_INT4_G32 (PuzzleKV section 1 and 4: factors stored in
+ * int4; ranks up to 16): lk/rk/lv hold the factors' codes in the element order
+ * above and rv in rank quads, R_V^T as [rank_v/4][head_dim][4], two codes per
+ * byte (element 2i in the low nibble); lk_s/rk_s/lv_s/rv_s hold one fp16
+ * scale per 32 consecutive elements of one page's factor, [batch][kv_heads]
+ * [max_pages][elements / 32], with the latent codec of lrkv_append_latent
+ * (symmetric codes in [-7, 7], s16 = fp16(amax / 7)). lrkv_factor_page
+ * quantises L first and forms R = L_hat^T X from the dequantised L_hat. The
+ * code arrays must be 16-byte aligned (INVALID_ARG otherwise).
+ *
  * A factored page holds X_hat = L R (PuzzleKV Eq. 2: L = the page's top left
  * singular vectors, R = Sigma W^T). Key-side arrays are stored as L and R, the
  * value side transposed (dimension-major), as are the dense values: each decode
@@ -139,6 +149,8 @@ typedef struct lrkv_paged_cache {
     void *lk, *rk, *lv, *rv;
     int32_t *page_table;  /* device                                             */
     int32_t *lens;        /* device int32 [batch]                               */
+    int32_t factor_fmt;   /* lrkv_fmt of lk/rk/lv/rv (dense pages stay fp16)    */
+    void *lk_s, *rk_s, *lv_s, *rv_s;   /* int4 factor scales; NULL for fp16     */
 } lrkv_paged_cache;
 
 /* Human-readable name of a status code (static string). */

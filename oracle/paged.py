@@ -25,6 +25,14 @@ Readings (the pages are silent or cut off):
 * the value side of a factored page (the text stops after the key-side score)
   is (a_p L^V) R^V by associativity, never forming V_hat.
 * eigen-order is descending, ties broken towards the lower index.
+* int4 factors (PuzzleKV, contributions list and section 4, "per-factor INT4
+  quantisation"; no grouping or order is given): each factor of a page is
+  quantised with the latent codec (symmetric codes in [-7, 7], one fp16 scale
+  per 32 consecutive elements) in its stored element order: keys L [P][r] and
+  R [r][d] row-major, values L^T [r][P] and R^T in rank quads [r/4][d][4]. L is
+  quantised first and R = L_hat^T X is formed from the dequantised L_hat, so
+  that R absorbs the error of L (the least-squares R for the stored L_hat when
+  L_hat has orthonormal columns).
 """
 from __future__ import annotations
 
@@ -32,6 +40,7 @@ import math
 
 import numpy as np
 
+from . import codec
 from .attn import chunk_partials, merge_partials
 
 
@@ -157,6 +166,51 @@ def factor_jacobi(X: np.ndarray, r: int, tol: float = 1e-14, max_sweeps: int = 3
     w, V, _ = jacobi_eigh(X @ X.T, tol, max_sweeps)
     Q = _top_eigvecs(w, V, r)
     return Q, Q.T @ X
+
+
+# ----------------------------------------------------------------------------- int4 factors
+
+FACTOR_LAYOUTS = ("key_L", "key_R", "value_L", "value_R")
+
+
+def stored_index(layout: str, rows: int, cols: int) -> np.ndarray:
+    """idx with stored[e] = F.flat[idx[e]] for the logical factor F [rows][cols]
+    (L [P][r] or R [r][d]) in the stored element order of ``layout``."""
+    e = np.arange(rows * cols)
+    if layout in ("key_L", "key_R"):
+        return e                                        # row-major as is
+    if layout == "value_L":                             # L^T [r][P]: e = k P + t
+        k, t = e // rows, e % rows
+        return t * cols + k
+    if layout == "value_R":                             # rank quads: e = (k/4) 4d + 4 dim + k%4
+        if rows % 4:
+            raise ValueError("value R needs a rank that is a multiple of 4")
+        k = 4 * (e // (4 * cols)) + e % 4
+        dim = (e // 4) % cols
+        return k * cols + dim
+    raise ValueError(layout)
+
+
+def quantize_factor(F: np.ndarray, layout: str):
+    """Quantise one page factor F (logical shape) in its stored order.
+    -> (codes int8 [n] in stored order, scales float16 [n/32], F_hat float64 logical)."""
+    F = np.asarray(F)
+    idx = stored_index(layout, *F.shape)
+    codes, scales = codec.quantize(F.astype(np.float32).reshape(-1)[idx])
+    F_hat = np.empty(F.size)
+    F_hat[idx] = codec.dequantize(codes, scales).astype(np.float64)
+    return codes, scales, F_hat.reshape(F.shape)
+
+
+def factor_int4(X: np.ndarray, r: int, side: str):
+    """int4 factors of one page (``side`` "key" or "value"): L from the Gram route,
+    quantised; R = L_hat^T X, quantised. -> (L_hat, R_hat, (L codes, L scales),
+    (R codes, R scales)), codes in stored order."""
+    X = np.asarray(X, np.float64)
+    L, _ = factor_gram(X, r)
+    Lc, Ls, L_hat = quantize_factor(L, side + "_L")
+    Rc, Rs, R_hat = quantize_factor(L_hat.T @ X, side + "_R")
+    return L_hat, R_hat, (Lc, Ls), (Rc, Rs)
 
 
 # ----------------------------------------------------------------------------- attention

@@ -52,6 +52,7 @@ class PagedCacheDesc(ctypes.Structure):
         ("rank_k", c_i32), ("rank_v", c_i32), ("max_pages", c_i32),
         ("dense_k", c_vp), ("dense_v", c_vp), ("lk", c_vp), ("rk", c_vp), ("lv", c_vp), ("rv", c_vp),
         ("page_table", c_vp), ("lens", c_vp),
+        ("factor_fmt", c_i32), ("lk_s", c_vp), ("rk_s", c_vp), ("lv_s", c_vp), ("rv_s", c_vp),
     ]
 
 

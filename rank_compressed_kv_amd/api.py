@@ -233,7 +233,7 @@ class PagedCache:
 
     def __init__(self, batch: int, kv_heads: int, q_per_kv: int, head_dim: int = 128,
                  page_size: int = 32, sink_pages: int = 1, window_pages: int = 4, rank_k: int = 12,
-                 rank_v: int = 12, max_pages: int = 1024, device="cuda"):
+                 rank_v: int = 12, max_pages: int = 1024, device="cuda", factor_fmt: int = FMT_FP16):
         self.B, self.H, self.G, self.d, self.P = batch, kv_heads, q_per_kv, head_dim, page_size
         self.sink, self.window, self.rk_, self.rv_, self.max_pages = sink_pages, window_pages, rank_k, rank_v, max_pages
         dev = torch.device(device)
@@ -242,17 +242,39 @@ class PagedCache:
         # keys row-major; values (dense and factored) dimension-major
         self.dense_k = torch.zeros((batch, kv_heads, nd, page_size, head_dim), dtype=f16, device=dev)
         self.dense_v = torch.zeros((batch, kv_heads, nd, head_dim, page_size), dtype=f16, device=dev)
-        self.lk = torch.zeros((batch, kv_heads, max_pages, page_size, rank_k), dtype=f16, device=dev)
-        self.rk = torch.zeros((batch, kv_heads, max_pages, rank_k, head_dim), dtype=f16, device=dev)
-        self.lv = torch.zeros((batch, kv_heads, max_pages, rank_v, page_size), dtype=f16, device=dev)
-        self.rv = torch.zeros((batch, kv_heads, max_pages, head_dim, rank_v), dtype=f16, device=dev)
+        self.factor_fmt = factor_fmt
+        if factor_fmt == FMT_FP16:
+            self.lk = torch.zeros((batch, kv_heads, max_pages, page_size, rank_k), dtype=f16, device=dev)
+            self.rk = torch.zeros((batch, kv_heads, max_pages, rank_k, head_dim), dtype=f16, device=dev)
+            self.lv = torch.zeros((batch, kv_heads, max_pages, rank_v, page_size), dtype=f16, device=dev)
+            self.rv = torch.zeros((batch, kv_heads, max_pages, head_dim, rank_v), dtype=f16, device=dev)
+            self.lk_s = self.rk_s = self.lv_s = self.rv_s = None
+        elif factor_fmt == FMT_INT4_G32:
+            # codes, two per byte, in the fp16 layouts' element order; one fp16 scale
+            # per 32 consecutive elements of a page's factor
+            u8 = torch.uint8
+            nl_k, nr_k = page_size * rank_k, rank_k * head_dim
+            nl_v, nr_v = page_size * rank_v, rank_v * head_dim
+            shp = (batch, kv_heads, max_pages)
+            self.lk = torch.zeros(shp + (nl_k // 2,), dtype=u8, device=dev)
+            self.rk = torch.zeros(shp + (nr_k // 2,), dtype=u8, device=dev)
+            self.lv = torch.zeros(shp + (nl_v // 2,), dtype=u8, device=dev)
+            self.rv = torch.zeros(shp + (nr_v // 2,), dtype=u8, device=dev)
+            self.lk_s = torch.zeros(shp + (nl_k // 32,), dtype=f16, device=dev)
+            self.rk_s = torch.zeros(shp + (nr_k // 32,), dtype=f16, device=dev)
+            self.lv_s = torch.zeros(shp + (nl_v // 32,), dtype=f16, device=dev)
+            self.rv_s = torch.zeros(shp + (nr_v // 32,), dtype=f16, device=dev)
+        else:
+            raise ValueError("factor_fmt must be FMT_FP16 or FMT_INT4_G32")
         self.page_table = torch.full((batch, kv_heads, max_pages), PAGE_EMPTY, dtype=torch.int32, device=dev)
         self.lens = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.host_lens = np.zeros(batch, dtype=np.int64)
         self.desc = PagedCacheDesc(batch, kv_heads, q_per_kv, head_dim, page_size, sink_pages, window_pages,
                                    rank_k, rank_v, max_pages, self.dense_k.data_ptr(), self.dense_v.data_ptr(),
                                    self.lk.data_ptr(), self.rk.data_ptr(), self.lv.data_ptr(),
-                                   self.rv.data_ptr(), self.page_table.data_ptr(), self.lens.data_ptr())
+                                   self.rv.data_ptr(), self.page_table.data_ptr(), self.lens.data_ptr(),
+                                   factor_fmt, *(0 if t is None else t.data_ptr()
+                                                 for t in (self.lk_s, self.rk_s, self.lv_s, self.rv_s)))
 
     @property
     def max_len(self) -> int:

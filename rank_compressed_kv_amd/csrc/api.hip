@@ -130,6 +130,12 @@ static int32_t check_paged(const lrkv_paged_cache* c) {
     if (c->max_pages > 64 * kMaxSplit) return LRKV_ERR_UNSUPPORTED;
     if (!aligned16(c->dense_k) || !aligned16(c->dense_v) || !aligned16(c->rk) || !aligned16(c->rv))
         return LRKV_ERR_INVALID_ARG;
+    if (c->factor_fmt != LRKV_FMT_FP16 && c->factor_fmt != LRKV_FMT_INT4_G32) return LRKV_ERR_INVALID_ARG;
+    if (c->factor_fmt == LRKV_FMT_INT4_G32 && (!c->lk_s || !c->rk_s || !c->lv_s || !c->rv_s))
+        return LRKV_ERR_INVALID_ARG;
+    if (c->factor_fmt == LRKV_FMT_INT4_G32 && (c->rank_k > 16 || c->rank_v > 16)) return LRKV_ERR_UNSUPPORTED;
+    // int4 factor codes are written as 16-byte groups
+    if (c->factor_fmt == LRKV_FMT_INT4_G32 && (!aligned16(c->lk) || !aligned16(c->lv))) return LRKV_ERR_INVALID_ARG;
     return LRKV_OK;
 }
 

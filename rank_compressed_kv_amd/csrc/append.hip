@@ -80,28 +80,6 @@ __global__ __launch_bounds__(256) void append_fp16_small(const float* __restrict
     for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] += n_new;
 }
 
-// The codec of one 32-element group: fp16 scale and the 32 codes.
-__device__ void quant_group(const float* __restrict__ x, int* codes, half_t* scale) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(x[k]));
-    const float s32 = amax / 7.0f;                       // IEEE fp32 division
-    half_t s16 = (half_t)s32;                            // round to nearest even
-    if (__builtin_isinf((float)s16)) s16 = (half_t)65504.0f;
-    const double den = (double)(float)s16;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-        int c = 0;
-        if (den != 0.0) {
-            double qd = rint((double)x[k] / den);        // fp64 quotient, half-even
-            qd = fmin(7.0, fmax(-7.0, qd));
-            c = (int)qd;
-        }
-        codes[k] = c;
-    }
-    *scale = s16;
-}
-
 // Keys: one thread per (b, u, i, group). 16 packed bytes + one scale.
 __global__ void append_int4_k(const float* __restrict__ nk, uint8_t* __restrict__ hk,
                               half_t* __restrict__ sk, const int32_t* __restrict__ lens, int B,

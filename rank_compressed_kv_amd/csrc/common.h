@@ -55,6 +55,30 @@ __device__ __forceinline__ int nibble(uint32_t w, int k) {
     return ((int)(w << (28 - 4 * k))) >> 28;
 }
 
+// ---------------------------------------------------------------- int4 codec
+// The symmetric int4 codec of one 32-element group (documented in lrkv.h): fp16
+// scale and the 32 codes. Shared by the latent append and the page factors.
+__device__ inline void quant_group(const float* __restrict__ x, int* codes, half_t* scale) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    const float s32 = amax / 7.0f;                       // IEEE fp32 division
+    half_t s16 = (half_t)s32;                            // round to nearest even
+    if (__builtin_isinf((float)s16)) s16 = (half_t)65504.0f;
+    const double den = (double)(float)s16;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        int c = 0;
+        if (den != 0.0) {
+            double qd = rint((double)x[k] / den);        // fp64 quotient, half-even
+            qd = fmin(7.0, fmax(-7.0, qd));
+            c = (int)qd;
+        }
+        codes[k] = c;
+    }
+    *scale = s16;
+}
+
 // ---------------------------------------------------------------- launch plumbing
 struct Status {
     static int32_t from_hip(hipError_t e) { return e == hipSuccess ? LRKV_OK : LRKV_ERR_HIP; }

@@ -25,14 +25,12 @@
 // Factored pages stream through three register buffers (two pages in flight
 // while one is computed); dense pages (sink and window, a handful per
 // sequence) are handled after them without pipelining.
-#include "common.h"
+#include "tiles.h"
 
 #include <math.h>
 
 namespace lrkv {
 namespace {
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ floatx4 mfma16k16(half4 a, half4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -50,6 +48,28 @@ __device__ __forceinline__ half8 ld8(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ half4 ld4(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+__device__ __forceinline__ uint4 ldw4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ldh(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// Four int4 codes (16 bits: code i at bits 4 i) times their fp16 scale, in the
+// order 0, 2, 1, 3: the two bytes are spread to the two 16-bit halves, and the
+// low / high nibbles masked into the mantissa of 1024.0 (exact integers).
+__device__ __forceinline__ half4 decode4(uint32_t w16, uint32_t scale_bits) {
+    const uint32_t x = (w16 ^ 0x8888u), y = __builtin_amdgcn_perm(0u, x, 0x0C010C00u);
+    const uint32_t magic = 0x64006400u;
+    const half2_t lo_off = {-1032.0f16, -1032.0f16};
+    const half2_t hi_mul = {0.0625f16, 0.0625f16}, hi_off = {-72.0f16, -72.0f16};
+    const half2_t s2 = __builtin_bit_cast(half2_t, scale_bits * 0x00010001u);
+    const half2_t a = (__builtin_bit_cast(half2_t, and_or(y, 0x000F000Fu, magic)) + lo_off) * s2;
+    const half2_t b = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(y, 0x00F000F0u, magic)), hi_mul, hi_off) * s2;
+    return half4{a[0], a[1], b[0], b[1]};
+}
+// the order decode4 yields: element e is code pi4(e)
+__host__ __device__ constexpr int pi4(int e) { return e == 1 ? 2 : e == 2 ? 1 : e; }
 
 // max / sum over the four lane groups (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float xg_max(float v) {
@@ -77,6 +97,7 @@ __device__ __forceinline__ void split4(floatx4 v, half4& hi, half4& lo) {
 
 struct HybridArgs {
     const half_t *dk, *dv, *lk, *rk, *lv, *rv;
+    const half_t *lks, *rks, *lvs, *rvs;   // int4 factor scales
     const int32_t* table;
     const int32_t* lens;
     const float* q;       // [B][Hq][128]
@@ -95,7 +116,24 @@ struct FPage {
     half4 rv[8][NV];      // R_V^T[16 mb + c][16 rb + 4 g + 0..3]
 };
 
-template <int NK, int NV>
+// int4 factors (ranks <= 16): the codes of one page for this lane, and their scales.
+// R_K: the 16 bytes of dims [32 g, 32 g + 32) of rank row c (K step s takes dims
+// 32 g + 8 s + ...; one scale); L_K: ranks 4 g .. 4 g + 3 of tokens c and 16 + c;
+// L_V^T: tokens 16 tb + 4 g .. + 3 of rank row c (one scale); R_V^T (rank quads):
+// the 16 bytes of quad g at dims 8 c .. 8 c + 7 (dim block mb takes dim 8 c + mb;
+// one scale).
+struct FPage4 {
+    uint4 rk;
+    uint32_t rks;
+    uint32_t lk[2], lks[2];
+    uint32_t lv[2], lvs;
+    uint4 rv;
+    uint32_t rvs;
+};
+template <bool I4, int NK, int NV> struct PageOf { using T = FPage<NK, NV>; };
+template <int NK, int NV> struct PageOf<true, NK, NV> { using T = FPage4; };
+
+template <int NK, int NV, bool I4>
 __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const HybridArgs a) {
     constexpr int D = 128, P = 32;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), l = threadIdx.x & 63;
@@ -127,7 +165,10 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float v = c < a.G ? qs[32 * s + 8 * g + j] * a.qscale : 0.0f;
+                // int4 factors: K step s, lane group g takes dims 32 g + 8 s + (the code
+                // unpack order 0, 4, 1, 5, 2, 6, 3, 7)
+                const int dim = I4 ? 32 * g + 8 * s + code_pos_inv(j) : 32 * s + 8 * g + j;
+                const float v = c < a.G ? qs[dim] * a.qscale : 0.0f;
                 qh[s][j] = (half_t)v;
                 ql[s][j] = (half_t)(v - (float)qh[s][j]);
             }
@@ -139,6 +180,43 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
     const rsrc_t rs_lk = make_rs(a.lk + bhp * P * rk, (uint32_t)(a.max_pages * P * rk * 2));
     const rsrc_t rs_lv = make_rs(a.lv + bhp * P * rv, (uint32_t)(a.max_pages * P * rv * 2));
     const rsrc_t rs_rv = make_rs(a.rv + bhp * rv * D, (uint32_t)(a.max_pages * rv * D * 2));
+
+    // int4 factors: codes and scales of this (sequence, KV head); page strides in bytes
+    const uint32_t s_rk = rk * D / 2, s_lk = P * rk / 2, s_lv = P * rv / 2, s_rv = rv * D / 2;
+    rsrc_t q_rk, q_lk, q_lv, q_rv, q_rks, q_lks, q_lvs, q_rvs;
+    uint32_t p_rk = kOff, p_lk0 = kOff, p_lk1 = kOff, p_lv0 = kOff, p_lv1 = kOff, p_rv = kOff;
+    uint32_t p_rks = kOff, p_lks0 = kOff, p_lks1 = kOff, p_lvs = kOff, p_rvs = kOff;
+    if constexpr (I4) {
+        const uint32_t mp = (uint32_t)a.max_pages;
+        q_rk = make_rs((const uint8_t*)a.rk + bhp * s_rk, mp * s_rk);
+        q_lk = make_rs((const uint8_t*)a.lk + bhp * s_lk, mp * s_lk);
+        q_lv = make_rs((const uint8_t*)a.lv + bhp * s_lv, mp * s_lv);
+        q_rv = make_rs((const uint8_t*)a.rv + bhp * s_rv, mp * s_rv);
+        q_rks = make_rs(a.rks + bhp * (s_rk / 16), mp * (s_rk / 8));
+        q_lks = make_rs(a.lks + bhp * (s_lk / 16), mp * (s_lk / 8));
+        q_lvs = make_rs(a.lvs + bhp * (s_lv / 16), mp * (s_lv / 8));
+        q_rvs = make_rs(a.rvs + bhp * (s_rv / 16), mp * (s_rv / 8));
+        // one scale per 32 stored elements (16 code bytes): scale byte = code byte / 8
+        if (c < rk) {
+            p_rk = c * 64 + 16 * g;                      // R_K[c][32 g .. 32 g + 31]
+            p_rks = p_rk / 8;
+        }
+        if (4 * g < rk) {
+            p_lk0 = (c * rk + 4 * g) / 2;                // L_K[c][4 g .. 4 g + 3]
+            p_lk1 = ((16 + c) * rk + 4 * g) / 2;         // L_K[16 + c][4 g .. 4 g + 3]
+            p_lks0 = p_lk0 / 16 * 2;
+            p_lks1 = p_lk1 / 16 * 2;
+        }
+        if (c < rv) {
+            p_lv0 = 16 * c + 2 * g;                      // L_V^T[c][4 g .. 4 g + 3]
+            p_lv1 = 16 * c + 8 + 2 * g;                  // L_V^T[c][16 + 4 g .. 16 + 4 g + 3]
+            p_lvs = 2 * c;
+        }
+        if (4 * g < rv) {
+            p_rv = 256 * g + 16 * c;                     // quad g, dims 8 c .. 8 c + 7
+            p_rvs = p_rv / 8;
+        }
+    }
 
     // per-lane offsets inside a page (kOff: masked lane), added to the page base
     uint32_t o_rk[NK], o_lk[NK], o_lv[NV], o_rv[NV];
@@ -156,7 +234,8 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
     // Loads of the next factored page (its bit leaves `mask`); with none left,
     // every load reads past the buffers (zeros), so the load count per page is
     // fixed.
-    auto fetch = [&](FPage<NK, NV>& f, uint64_t& mask) __attribute__((always_inline)) {
+    using Page = typename PageOf<I4, NK, NV>::T;
+    auto fetch = [&](Page& f, uint64_t& mask) __attribute__((always_inline)) {
         uint32_t slot = 0, none = kOff;
         if (mask) {
             const int bit = __builtin_ctzll(mask);
@@ -164,6 +243,19 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
             slot = (uint32_t)__builtin_amdgcn_readlane(entry, bit);
             none = 0;
         }
+        if constexpr (I4) {
+            f.rk = ldw4(q_rk, none | (slot * s_rk + p_rk));
+            f.rks = ldh(q_rks, none | (slot * (s_rk / 8) + p_rks));
+            f.lk[0] = ldh(q_lk, none | (slot * s_lk + p_lk0));
+            f.lk[1] = ldh(q_lk, none | (slot * s_lk + p_lk1));
+            f.lks[0] = ldh(q_lks, none | (slot * (s_lk / 8) + p_lks0));
+            f.lks[1] = ldh(q_lks, none | (slot * (s_lk / 8) + p_lks1));
+            f.lv[0] = ldh(q_lv, none | (slot * s_lv + p_lv0));
+            f.lv[1] = ldh(q_lv, none | (slot * s_lv + p_lv1));
+            f.lvs = ldh(q_lvs, none | (slot * (s_lv / 8) + p_lvs));
+            f.rv = ldw4(q_rv, none | (slot * s_rv + p_rv));
+            f.rvs = ldh(q_rvs, none | (slot * (s_rv / 8) + p_rvs));
+        } else {
 #pragma unroll
         for (int rb = 0; rb < NK; ++rb) {
             const uint32_t base = none | (slot * rk * D * 2);
@@ -182,6 +274,7 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) f.rv[mb][rb] = ld4(rs_rv, (base + o_rv[rb] + 32 * rv * mb) | (o_rv[rb] & kOff));
         }
+        }
     };
 
     float m_run = -INFINITY, l_lane = 0.0f;
@@ -191,7 +284,8 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
 
     // Online softmax of one page's scores (lane: head c, tokens 16 tb + 4 g + i;
     // tokens >= ntok masked); returns p as the next MFMA's B operand.
-    auto softmax = [&](const floatx4* S, int ntok, half4* pb) __attribute__((always_inline)) {
+    // perm: pack p in the order pi4 (the token order of int4 L_V^T fragments)
+    auto softmax = [&](const floatx4* S, int ntok, half4* pb, bool perm) __attribute__((always_inline)) {
         float sv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) sv[k] = S[k >> 2][k & 3];
@@ -217,10 +311,47 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
         l_lane += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
-            pb[tb] = half4{(half_t)pr[4 * tb], (half_t)pr[4 * tb + 1], (half_t)pr[4 * tb + 2], (half_t)pr[4 * tb + 3]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pb[tb][i] = (half_t)pr[4 * tb + (perm ? pi4(i) : i)];
     };
 
-    auto factored = [&](const FPage<NK, NV>& f, int ntok) __attribute__((always_inline)) {
+    auto factored4 = [&](const FPage4& f, int ntok) __attribute__((always_inline)) {
+        const uint32_t magic = 0x64006400u;
+        const uint32_t rw[4] = {f.rk.x, f.rk.y, f.rk.z, f.rk.w};
+        floatx4 u = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const half8 ak = dequant_keys(rw[s], f.rks, magic);
+            u = mfma16(ak, qh[s], u);
+            u = mfma16(ak, ql[s], u);
+        }
+        // lane (c, g) holds U^T[4 g + i][c]; L_K fragments decode in rank order pi4
+        half4 uh, ul;
+        split4(floatx4{u[0], u[2], u[1], u[3]}, uh, ul);
+        floatx4 S[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const half4 lk = decode4(f.lk[tb], f.lks[tb]);
+            S[tb] = mfma16k16(lk, uh, floatx4{0.f, 0.f, 0.f, 0.f});
+            S[tb] = mfma16k16(lk, ul, S[tb]);
+        }
+        half4 pb[2];
+        softmax(S, ntok, pb, true);
+        floatx4 wt = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) wt = mfma16k16(decode4(f.lv[tb], f.lvs), pb[tb], wt);
+        const half4 wb = half4{(half_t)wt[0], (half_t)wt[2], (half_t)wt[1], (half_t)wt[3]};
+        const uint32_t vw[4] = {f.rv.x, f.rv.y, f.rv.z, f.rv.w};
+        // dim block mb: A row c is dim 8 c + mb (the 16-bit half mb of the lane's run)
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) o[mb] = mfma16k16(decode4(vw[mb >> 1] >> (16 * (mb & 1)), f.rvs), wb, o[mb]);
+    };
+
+    auto factored = [&](const Page& f, int ntok) __attribute__((always_inline)) {
+        if constexpr (I4) {
+            factored4(f, ntok);
+            return;
+        } else {
         half4 uh[NK], ul[NK];
 #pragma unroll
         for (int rb = 0; rb < NK; ++rb) {
@@ -243,7 +374,7 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
             }
         }
         half4 pb[2];
-        softmax(S, ntok, pb);
+        softmax(S, ntok, pb, false);
 #pragma unroll
         for (int rb = 0; rb < NV; ++rb) {
             floatx4 wt = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -252,6 +383,7 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
             const half4 wb = to_half4(wt);
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) o[mb] = mfma16k16(f.rv[mb][rb], wb, o[mb]);
+        }
         }
     };
 
@@ -263,7 +395,7 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
             run_mask &= run_mask - 1;
             return min(P, len - (p_begin + bit) * P);
         };
-        FPage<NK, NV> f0, f1, f2;
+        Page f0, f1, f2;
         fetch(f0, fetch_mask);
         fetch(f1, fetch_mask);
         while (run_mask) {
@@ -292,11 +424,24 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kf[tb][s] = ld8(rs_k, ((16 * tb + c) * D + 32 * s + 8 * g) * 2);
+            for (int s = 0; s < 4; ++s) {
+                if constexpr (I4) {
+                    // the queries' dim order: K step s, group g, element j = dim 32 g + 8 s + code_pos_inv(j)
+                    const half8 raw = ld8(rs_k, ((16 * tb + c) * D + 32 * g + 8 * s) * 2);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) kf[tb][s][j] = raw[code_pos_inv(j)];
+                } else {
+                    kf[tb][s] = ld8(rs_k, ((16 * tb + c) * D + 32 * s + 8 * g) * 2);
+                }
+            }
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) vf[mb][tb] = ld4(rs_v, ((16 * mb + c) * P + 16 * tb + 4 * g) * 2);
+            for (int tb = 0; tb < 2; ++tb) {
+                // A row c of dim block mb: dim 16 mb + c, or 8 c + mb with int4 factors
+                const int dim = I4 ? 8 * c + mb : 16 * mb + c;
+                vf[mb][tb] = ld4(rs_v, (dim * P + 16 * tb + 4 * g) * 2);
+            }
         floatx4 S[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
@@ -308,7 +453,7 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
             }
         }
         half4 pb[2];
-        softmax(S, ntok, pb);
+        softmax(S, ntok, pb, false);
         if (ntok < P) {
             // rows past the page's last token may hold anything; their p is zero
 #pragma unroll
@@ -336,13 +481,13 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ph[2 + 16 * mb + 4 * g + i] = o[mb][i];
+            for (int i = 0; i < 4; ++i) ph[2 + (I4 ? 8 * (4 * g + i) + mb : 16 * mb + 4 * g + i)] = o[mb][i];
     }
 }
 
-template <int NK, int NV>
+template <int NK, int NV, bool I4 = false>
 void launch_hybrid(const HybridArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((hybrid_decode<NK, NV>), dim3((a.n_waves + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((hybrid_decode<NK, NV, I4>), dim3((a.n_waves + 3) / 4), dim3(256), 0, st, a);
 }
 
 }  // namespace
@@ -353,13 +498,16 @@ int32_t launch_decode_hybrid(int phases, const lrkv_paged_cache* c, const float*
                              float* out, void* ws, const PagedWorkspace& w, hipStream_t st) {
     float* part = (float*)((char*)ws + w.part_off);
     HybridArgs a{(const half_t*)c->dense_k, (const half_t*)c->dense_v, (const half_t*)c->lk,
-                 (const half_t*)c->rk, (const half_t*)c->lv, (const half_t*)c->rv, c->page_table,
+                 (const half_t*)c->rk, (const half_t*)c->lv, (const half_t*)c->rv, (const half_t*)c->lk_s,
+                 (const half_t*)c->rk_s, (const half_t*)c->lv_s, (const half_t*)c->rv_s, c->page_table,
                  c->lens, q, part, c->batch, c->kv_heads, c->q_per_kv, c->sink_pages,
                  c->window_pages, c->rank_k, c->rank_v, c->max_pages, w.n_split,
                  w.pages_per_split, c->batch * c->kv_heads * w.n_split, sm_scale * kLog2e};
     if (phases & kPhasePartials) {
         const bool k2 = c->rank_k > 16, v2 = c->rank_v > 16;
-        if (!k2 && !v2) launch_hybrid<1, 1>(a, st);
+        // int4 factors: ranks <= 16 (checked with the cache description)
+        if (c->factor_fmt == LRKV_FMT_INT4_G32) launch_hybrid<1, 1, true>(a, st);
+        else if (!k2 && !v2) launch_hybrid<1, 1>(a, st);
         else if (!k2) launch_hybrid<1, 2>(a, st);
         else if (!v2) launch_hybrid<2, 1>(a, st);
         else launch_hybrid<2, 2>(a, st);

@@ -28,9 +28,11 @@ namespace {
 struct FactorArgs {
     const half_t *dk, *dv, *src_k, *src_v;
     half_t *lk, *rk, *lv, *rv;
+    half_t *lk_s, *rk_s, *lv_s, *rv_s;   // int4 factors: one scale per 32 stored elements
     int32_t* table;
     const int32_t* pages;
     int n_pages, B, H, P, sink, window, max_pages, rank_k, rank_v, src_len, max_sweeps;
+    bool int4;
 };
 
 // Resolves a (b, h, page) triple: returns false when it must be skipped; sets the
@@ -207,38 +209,121 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
     wave_sync_lds();
 
     const long bh = (long)b * a.H + h;
-    half_t* Lo = (is_v ? a.lv : a.lk) + (bh * a.max_pages + pg) * P * r;
-    half_t* Ro = (is_v ? a.rv : a.rk) + (bh * a.max_pages + pg) * (long)r * D;
-    // keys: L [P][r], R [r][D]; values transposed: L^T [r][P], R^T [D][r]
-    for (int e = l; e < P * r; e += 64) {
-        const int t = e / r, k = e % r;
-        const half_t v = (half_t)V[t][order[k]];
-        Lo[is_v ? k * P + t : e] = v;
-        Ls[k][t] = (float)v;
-    }
-    wave_sync_lds();
-    // R[k][d] = sum_t fp16(L[t][k]) X[t][d]: lane l owns dims l and l + 64
-    float x0[P], x1[P];
-#pragma unroll
-    for (int t = 0; t < P; ++t) {
-        x0[t] = (float)Xs[t][l];
-        x1[t] = (float)Xs[t][l + 64];
-    }
-    for (int k = 0; k < r; ++k) {
-        float s0 = 0.0f, s1 = 0.0f;
+    const long page = bh * a.max_pages + pg;
+    if (!a.int4) {
+        half_t* Lo = (is_v ? a.lv : a.lk) + page * P * r;
+        half_t* Ro = (is_v ? a.rv : a.rk) + page * (long)r * D;
+        // keys: L [P][r], R [r][D]; values transposed: L^T [r][P], R^T [D][r]
+        for (int e = l; e < P * r; e += 64) {
+            const int t = e / r, k = e % r;
+            const half_t v = (half_t)V[t][order[k]];
+            Lo[is_v ? k * P + t : e] = v;
+            Ls[k][t] = (float)v;
+        }
+        wave_sync_lds();
+        // R[k][d] = sum_t fp16(L[t][k]) X[t][d]: lane l owns dims l and l + 64
+        float x0[P], x1[P];
 #pragma unroll
         for (int t = 0; t < P; ++t) {
-            const float lt = Ls[k][t];
-            s0 = fmaf(lt, x0[t], s0);
-            s1 = fmaf(lt, x1[t], s1);
+            x0[t] = (float)Xs[t][l];
+            x1[t] = (float)Xs[t][l + 64];
         }
-        if (is_v) {
-            Ro[(long)l * r + k] = (half_t)s0;
-            Ro[(long)(l + 64) * r + k] = (half_t)s1;
-        } else {
-            Ro[(long)k * D + l] = (half_t)s0;
-            Ro[(long)k * D + l + 64] = (half_t)s1;
+        for (int k = 0; k < r; ++k) {
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int t = 0; t < P; ++t) {
+                const float lt = Ls[k][t];
+                s0 = fmaf(lt, x0[t], s0);
+                s1 = fmaf(lt, x1[t], s1);
+            }
+            if (is_v) {
+                Ro[(long)l * r + k] = (half_t)s0;
+                Ro[(long)(l + 64) * r + k] = (half_t)s1;
+            } else {
+                Ro[(long)k * D + l] = (half_t)s0;
+                Ro[(long)k * D + l + 64] = (half_t)s1;
+            }
         }
+        return;
+    }
+
+    // ---- int4 factors (r <= 16): quantise L in groups of 32 consecutive stored
+    // elements (one group per lane), then R = L_hat^T X from the dequantised L_hat,
+    // then R likewise. Stored orders: keys L [P][r], R [r][D]; values L^T [r][P],
+    // R^T in rank quads [r/4][D][4] (a decode lane's eight dims of one quad are
+    // then one 16-byte run with one scale).
+    uint8_t* Lc = (uint8_t*)(is_v ? a.lv : a.lk) + page * (P * r / 2);
+    uint8_t* Rc = (uint8_t*)(is_v ? a.rv : a.rk) + page * (r * D / 2);
+    half_t* Lsc = (is_v ? a.lv_s : a.lk_s) + page * (P * r / 32);
+    half_t* Rsc = (is_v ? a.rv_s : a.rk_s) + page * (r * D / 32);
+    auto store_group = [&](uint8_t* codes_out, half_t* scale_out, int j, const float* x, float* deq) {
+        int c[32];
+        half_t sc;
+        quant_group(x, c, &sc);
+        uint32_t wd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) v |= ((uint32_t)c[8 * q + n] & 0xFu) << (4 * n);
+            wd[q] = v;
+        }
+        *reinterpret_cast<uint4*>(codes_out + 16 * j) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        scale_out[j] = sc;
+        if (deq) {
+#pragma unroll
+            for (int n = 0; n < 32; ++n) deq[n] = (float)c[n] * (float)sc;
+        }
+    };
+    if (l < P * r / 32) {
+        float x[32], xd[32];
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {
+            const int e = 32 * l + n;
+            const int t = is_v ? e % P : e / r, k = is_v ? e / P : e % r;
+            x[n] = V[t][order[k]];
+        }
+        store_group(Lc, Lsc, l, x, xd);
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {
+            const int e = 32 * l + n;
+            const int t = is_v ? e % P : e / r, k = is_v ? e / P : e % r;
+            Ls[k][t] = xd[n];
+        }
+    }
+    wave_sync_lds();
+    // R (fp32) [r][D] into the eigenvector buffers, which are free now
+    float* Rs = &Vb[0][0][0];
+    {
+        float x0[P], x1[P];
+#pragma unroll
+        for (int t = 0; t < P; ++t) {
+            x0[t] = (float)Xs[t][l];
+            x1[t] = (float)Xs[t][l + 64];
+        }
+        for (int k = 0; k < r; ++k) {
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int t = 0; t < P; ++t) {
+                const float lt = Ls[k][t];
+                s0 = fmaf(lt, x0[t], s0);
+                s1 = fmaf(lt, x1[t], s1);
+            }
+            Rs[k * D + l] = s0;
+            Rs[k * D + l + 64] = s1;
+        }
+    }
+    wave_sync_lds();
+    if (l < r * D / 32) {
+        float x[32];
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {
+            const int e = 32 * l + n;
+            // keys R [r][D]; values in rank quads, [r/4][D][4]
+            const int k = is_v ? 4 * (e / (4 * D)) + e % 4 : e / D, d = is_v ? (e / 4) % D : e % D;
+            x[n] = Rs[k * D + d];
+        }
+        store_group(Rc, Rsc, l, x, nullptr);
     }
 }
 
@@ -259,9 +344,11 @@ int32_t launch_factor_page(const lrkv_paged_cache* c, const int32_t* pages, int 
                            hipStream_t st) {
     if (n_pages == 0) return LRKV_OK;
     FactorArgs a{(const half_t*)c->dense_k, (const half_t*)c->dense_v, src_k, src_v,
-                 (half_t*)c->lk, (half_t*)c->rk, (half_t*)c->lv, (half_t*)c->rv, c->page_table,
+                 (half_t*)c->lk, (half_t*)c->rk, (half_t*)c->lv, (half_t*)c->rv,
+                 (half_t*)c->lk_s, (half_t*)c->rk_s, (half_t*)c->lv_s, (half_t*)c->rv_s, c->page_table,
                  pages, n_pages, c->batch, c->kv_heads, c->page_size, c->sink_pages,
-                 c->window_pages, c->max_pages, c->rank_k, c->rank_v, src_len, max_sweeps};
+                 c->window_pages, c->max_pages, c->rank_k, c->rank_v, src_len, max_sweeps,
+                 c->factor_fmt == LRKV_FMT_INT4_G32};
     hipLaunchKernelGGL(factor_pages<128>, dim3(2 * n_pages), dim3(64), 0, st, a);
     hipLaunchKernelGGL(mark_factored, dim3((n_pages + 255) / 256), dim3(256), 0, st, a);
     return last_launch_status();

@@ -50,7 +50,7 @@ def _latent(**kw):
 def _paged(**kw):
     f = dict(batch=2, kv_heads=2, q_per_kv=4, head_dim=128, page_size=32, sink_pages=1, window_pages=4,
              rank_k=12, rank_v=12, max_pages=64, dense_k=FAKE, dense_v=FAKE, lk=FAKE, rk=FAKE, lv=FAKE,
-             rv=FAKE, page_table=FAKE, lens=FAKE)
+             rv=FAKE, page_table=FAKE, lens=FAKE, factor_fmt=0, lk_s=None, rk_s=None, lv_s=None, rv_s=None)
     f.update(kw)
     return L.PagedCacheDesc(*[f[n] for n, _ in L.PagedCacheDesc._fields_])
 
@@ -111,6 +111,13 @@ def test_paged_validation(lib):
         assert lib.lrkv_factor_page(ctypes.byref(bad), ok, 3, None, None, 0, 0, None) == L.LRKV_ERR_UNSUPPORTED, kw
         assert lib.lrkv_decode_workspace_bytes(2, ctypes.byref(bad), 1000, 0) == 0, kw
     assert lib.lrkv_decode_workspace_bytes(2, ctypes.byref(_paged(q_per_kv=16, rank_k=32, rank_v=4)), 1000, 0) > 0
+    # int4 factors need their four scale arrays; unknown formats are invalid
+    i4 = dict(factor_fmt=1, lk_s=FAKE, rk_s=FAKE, lv_s=FAKE, rv_s=FAKE)
+    assert lib.lrkv_decode_workspace_bytes(2, ctypes.byref(_paged(**i4)), 1000, 0) > 0
+    assert lib.lrkv_decode_workspace_bytes(2, ctypes.byref(_paged(**dict(i4, rv_s=None))), 1000, 0) == 0
+    assert lib.lrkv_decode_workspace_bytes(2, ctypes.byref(_paged(factor_fmt=2)), 1000, 0) == 0
+    bad = _paged(**dict(i4, lk_s=None))
+    assert lib.lrkv_factor_page(ctypes.byref(bad), ok, 3, None, None, 0, 0, None) == L.LRKV_ERR_INVALID_ARG
     need = lib.lrkv_decode_workspace_bytes(2, ctypes.byref(d), 1000, 0)
     assert need > 0
     assert lib.lrkv_decode_attn(2, ctypes.byref(d), ok, ok, None, 0.0, ok, ok, need, 1000, 0, None) == L.LRKV_ERR_INVALID_ARG

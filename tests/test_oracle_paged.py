@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import accounting, attn, paged
+from oracle import accounting, attn, codec, paged
 
 
 def test_page_table_closed_form_matches_replay():
@@ -150,3 +150,84 @@ def test_synth_paged_pages_are_low_rank():
     # noise singular values of a 32 x 128 N(0, 0.05^2) block lie near 0.05 (sqrt(128) +- sqrt(32))
     assert 0.05 * (np.sqrt(128) - np.sqrt(32)) * 0.8 < S[12:].min()
     assert S[12] < 0.05 * (np.sqrt(128) + np.sqrt(32)) * 1.2
+
+
+# ----------------------------------------------------------------------------- int4 page factors
+
+def _f16_scale(amax):
+    return np.float16(np.float32(amax) / np.float32(7.0))
+
+
+def test_int4_factor_groups_closed_form():
+    """Each stored layout groups the elements the header documents: with F increasing
+    in both indices the amax of every group is one known element, so the scales have a
+    closed form, and every dequantised element sits within half its own group's scale."""
+    cases = {
+        # layout: (rows, cols, F[i][j], group of element (i, j), amax of group g)
+        "key_L": (32, 8, lambda t, k: 1 + k + 100 * t, lambda t, k: t // 4, lambda g: 8 + 100 * (4 * g + 3)),
+        "key_R": (8, 128, lambda k, d: 1 + d + 1000 * k, lambda k, d: 4 * k + d // 32,
+                  lambda g: 1 + 32 * (g % 4) + 31 + 1000 * (g // 4)),
+        "value_L": (32, 12, lambda t, k: 1 + t + 100 * k, lambda t, k: k, lambda g: 32 + 100 * g),
+        "value_R": (12, 128, lambda k, d: 1 + d + 1000 * k, lambda k, d: 16 * (k // 4) + d // 8,
+                    lambda g: 1 + 8 * (g % 16) + 7 + 1000 * (4 * (g // 16) + 3)),
+    }
+    for layout, (rows, cols, f, grp, amax) in cases.items():
+        F = np.fromfunction(np.vectorize(f), (rows, cols), dtype=np.int64).astype(np.float64)
+        codes, scales, F_hat = paged.quantize_factor(F, layout)
+        n_groups = rows * cols // 32
+        assert codes.shape == (rows * cols,) and scales.shape == (n_groups,)
+        expect = np.array([_f16_scale(amax(g)) for g in range(n_groups)], np.float16)
+        np.testing.assert_array_equal(scales, expect, err_msg=layout)
+        for i in range(rows):
+            for j in range(cols):
+                s = float(scales[grp(i, j)])
+                assert abs(F_hat[i, j] - F[i, j]) <= s / 2 + 1e-12, (layout, i, j)
+        # the group's amax element is coded +-7
+        assert np.all(np.max(np.abs(codes.reshape(n_groups, 32)), axis=1) == 7)
+
+
+def test_int4_factor_R_formed_from_dequantised_L():
+    """A page whose rows t_k = 3 + 3k are orthogonal (disjoint 8-dim supports, distinct
+    norms): L = +-e_{t_k} exactly, every nonzero of L is coded 7 with scale fp16(1/7), so
+    L_hat = +-c e_{t_k}, c = 7 fp16(1/7). R = L_hat^T X has rows +-c X[t_k], whose eight
+    nonzeros form one group; hence X_hat row t_k = c dq(q(c X[t_k])) (sign-free, the codec
+    being odd). With R taken from L instead, or L left unquantised, the result differs."""
+    base = np.array([7, 2.5, -3.5, 1.5, 0.5, -6.5, 4.5, 5.5])
+    X = np.zeros((32, 128))
+    rows = {}
+    for k in range(8):
+        t = 3 + 3 * k
+        X[t, 8 * k:8 * k + 8] = base * (1 + k / 4)
+        rows[t] = slice(8 * k, 8 * k + 8)
+    c = 7.0 * float(np.float16(np.float32(1.0) / np.float32(7.0)))
+
+    def qdq(v):
+        g = np.zeros(32, np.float32)
+        g[:8] = v
+        cd, sc = codec.quantize(g)
+        return codec.dequantize(cd, sc)[:8].astype(np.float64)
+
+    expect = np.zeros_like(X)
+    alt = np.zeros_like(X)
+    for t, sl in rows.items():
+        expect[t, sl] = c * qdq(c * X[t, sl])
+        alt[t, sl] = c * qdq(X[t, sl])
+    assert np.any(expect != alt)
+    for side in ("key", "value"):
+        L_hat, R_hat, (Lc, Ls), _ = paged.factor_int4(X, 8, side)
+        assert set(np.unique(np.abs(L_hat))) <= {0.0, c}
+        np.testing.assert_array_equal(L_hat @ R_hat, expect, err_msg=side)
+
+
+def test_int4_factor_error_bound_random_page():
+    """A low-rank-plus-noise page: the int4 factors reconstruct X within the rank-r
+    optimum plus the first-order effect of the two quantisation errors."""
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((32, 12)) @ rng.standard_normal((12, 128)) / np.sqrt(12) + 0.05 * rng.standard_normal((32, 128))
+    for side in ("key", "value"):
+        L_hat, R_hat, (Lc, Ls), (Rc, Rs) = paged.factor_int4(X, 12, side)
+        eL = 0.5 * np.sqrt(32 * np.sum(Ls.astype(np.float64) ** 2))
+        eR = 0.5 * np.sqrt(32 * np.sum(Rs.astype(np.float64) ** 2))
+        bound = paged.optimal_error(X, 12) + (2 * eL + eL ** 2) * np.linalg.norm(X, 2) + (1 + eL) * eR
+        assert np.linalg.norm(X - L_hat @ R_hat) <= bound
+        assert np.max(np.abs(R_hat - L_hat.T @ X)) <= 0.5 * np.max(Rs.astype(np.float64)) + 1e-12
