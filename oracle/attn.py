@@ -11,6 +11,10 @@ Definitions written out plainly:
   (Palu digest, Method details: G-LRD reconstruction, value fusion, RoPE).
 * absorbed-query path (no RoPE): scores = H^k q' with q' = q (B^k)^T
   (Palu digest, Method details: key fusion).
+* chunked prefill: a chunk of new tokens is appended, then each of its queries
+  attends causally over the cache up to its own position (the multi-query form
+  of the reconstruct-with-RoPE path; the pages describe the prefill workflow
+  but print no prefill kernel, so this is the plain causal reading).
 
 Layout and indexing readings (the pages are silent):
 
@@ -86,6 +90,37 @@ def palu_decode(hk, hv, Bk, q, lens, s: int, g_q: int, d_h: int, theta: float,
             out[b, j], p = softmax_attention(qr, Kr, hv[b, u, :T], scale)
             probs[(b, j)] = p
     return (out, probs) if return_probs else out
+
+
+def palu_prefill(hk, hv, Bk, q, p0, s: int, g_q: int, d_h: int, theta: float, sm_scale=None):
+    """Chunked-prefill (multi-query) attention on the reconstruct-with-RoPE path.
+
+    The M new tokens of sequence b sit at positions p0[b] .. p0[b] + M - 1 of the
+    cache (appended before the call); query m attends causally, to tokens
+    0 .. p0[b] + m, exactly as one decode step at that length would (same
+    reconstruction, RoPE at each side's position, latent-space output).
+    hk, hv [B][U][T][r], Bk [U][r][s*d_h], q [B][M][Hq][d_h], p0 [B] ->
+    out [B][M][Hq][r].
+    """
+    hk = np.asarray(hk, np.float64)
+    hv = np.asarray(hv, np.float64)
+    Bk = np.asarray(Bk, np.float64)
+    q = np.asarray(q, np.float64)
+    Bsz, M, Hq = q.shape[0], q.shape[1], q.shape[2]
+    r = hk.shape[-1]
+    scale = 1.0 / np.sqrt(d_h) if sm_scale is None else sm_scale
+    out = np.zeros((Bsz, M, Hq, r))
+    for b in range(Bsz):
+        T = int(p0[b]) + M
+        pos = np.arange(T)
+        for j in range(Hq):
+            u, w = head_unit(j, s, g_q)
+            Kr = rope(hk[b, u, :T] @ Bk[u][:, w * d_h:(w + 1) * d_h], pos, theta)
+            for m in range(M):
+                n = int(p0[b]) + m + 1                                   # causal: tokens < n
+                qr = rope(q[b, m, j], n - 1, theta)
+                out[b, m, j], _ = softmax_attention(qr, Kr[:n], hv[b, u, :n], scale)
+    return out
 
 
 def palu_decode_absorbed(hk, hv, qa, lens, s: int, g_q: int, d_h: int, sm_scale=None):

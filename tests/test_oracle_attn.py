@@ -153,3 +153,45 @@ def test_layer_output_fused_equals_unfused():
     got = attn.layer_output_fused(o, fused)
     want = attn.layer_output_unfused(ps, [Hv] * Hq, Bv, Wo)
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_rows_equal_decode_at_each_length():
+    """Row m of a prefill chunk is one decode step at length p0 + m + 1 (causal reading);
+    an off-by-one in the mask or the query position fails it."""
+    rng = np.random.default_rng(21)
+    B, U, s, g_q, d_h, r, T, M = 2, 2, 2, 1, 16, 8, 40, 6
+    hk = rng.standard_normal((B, U, T, r))
+    hv = rng.standard_normal((B, U, T, r))
+    Bk = rng.standard_normal((U, r, s * d_h)) / 3
+    q = rng.standard_normal((B, M, U * s * g_q, d_h))
+    p0 = [T - M, 17]
+    out = attn.palu_prefill(hk, hv, Bk, q, p0, s, g_q, d_h, 1e4)
+    for m in range(M):
+        lens = [p0[0] + m + 1, p0[1] + m + 1]
+        ref = attn.palu_decode(hk, hv, Bk, q[:, m], lens, s, g_q, d_h, 1e4)
+        np.testing.assert_allclose(out[:, m], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_is_causal_and_brute_force():
+    """Tokens after a query's position do not change its row; a tiny case against the
+    pure-Python loops."""
+    rng = np.random.default_rng(22)
+    B, U, s, g_q, d_h, r, T, M = 1, 1, 1, 2, 8, 4, 12, 4
+    hk = rng.standard_normal((B, U, T, r))
+    hv = rng.standard_normal((B, U, T, r))
+    Bk = rng.standard_normal((U, r, s * d_h))
+    q = rng.standard_normal((B, M, 2, d_h))
+    p0 = [T - M]
+    out = attn.palu_prefill(hk, hv, Bk, q, p0, s, g_q, d_h, 100.0)
+    hk2, hv2 = hk.copy(), hv.copy()
+    hk2[:, :, T - 1] += 5.0
+    hv2[:, :, T - 1] -= 3.0
+    out2 = attn.palu_prefill(hk2, hv2, Bk, q, p0, s, g_q, d_h, 100.0)
+    np.testing.assert_allclose(out[:, :M - 1], out2[:, :M - 1], rtol=0, atol=0)
+    assert np.abs(out[:, M - 1] - out2[:, M - 1]).max() > 1e-3
+    for m in range(M):
+        n = p0[0] + m + 1
+        for j in range(2):
+            ref = brute.palu_decode_one(hk[0, 0, :n].tolist(), hv[0, 0, :n].tolist(), Bk[0].tolist(),
+                                        q[0, m, j].tolist(), 0, d_h, 100.0, n - 1, 1 / np.sqrt(d_h))
+            np.testing.assert_allclose(out[0, m, j], ref, rtol=1e-10, atol=1e-12)
