@@ -288,6 +288,36 @@ int32_t lrkv_paged_plan(const lrkv_paged_cache *cache, const int32_t *host_lens,
                         int32_t *out, int32_t max_out);
 
 /*
+ * Chunked-prefill attention on the reconstruct-with-RoPE path (Palu digest,
+ * Method details: K = H^k B^k rebuilt on chip, RoPE at each side's position,
+ * latent-space output o = p H^v). The m_tokens new tokens of each sequence
+ * must already be appended (lrkv_append_latent): token m of sequence b sits at
+ * position p0[b] + m, and its queries attend causally to tokens 0 .. p0[b] + m
+ * (positions are clamped to 0 .. lens[b] - 1).
+ *
+ *   cache    lrkv_latent_cache with fp16 latents, rank 256, head_dim 128 (any
+ *            kv_per_unit and q_per_kv; LRKV_ERR_UNSUPPORTED otherwise)
+ *   q        device float32 [batch][m_tokens][Hq][head_dim], un-rotated queries
+ *   bk       device fp16 [units][rank][kv_per_unit * head_dim] (B^k)
+ *   p0       device int32 [batch], the chunk's first position per sequence
+ *   host_max_len  the host's bound on p0[b] + m_tokens (1 .. capacity): sizes
+ *            the angle table and the key range
+ *   sm_scale softmax scale (<= 0 selects 1/sqrt(head_dim))
+ *   out      device float32 [batch][m_tokens][Hq][rank], 16-byte aligned
+ *   workspace device, at least lrkv_prefill_workspace_bytes(cache, m_tokens,
+ *            host_max_len) bytes (rotated queries and fp64-reduced angle tables),
+ *            else LRKV_ERR_WORKSPACE
+ *
+ * Enqueued on `stream`; nothing is allocated. INVALID_ARG for null or unaligned
+ * pointers and out-of-range sizes. lrkv_prefill_workspace_bytes returns 0 for
+ * invalid or unsupported arguments.
+ */
+size_t lrkv_prefill_workspace_bytes(const lrkv_latent_cache *cache, int32_t m_tokens, int32_t host_max_len);
+int32_t lrkv_prefill_attn(const lrkv_latent_cache *cache, const float *q, const void *bk, const int32_t *p0,
+                          int32_t m_tokens, int32_t host_max_len, float sm_scale, float *out, void *workspace,
+                          size_t ws_bytes, void *stream);
+
+/*
  * The projections on either side of the decode path (Palu digest, Method
  * details: a token is cached as its latents h = x A, and the value
  * up-projection B^v is fused offline into W^o, so the layer output is

@@ -29,7 +29,7 @@ EXPORTS = (
     "lrkv_status_string", "lrkv_version", "lrkv_decode_workspace_bytes", "lrkv_append_latent",
     "lrkv_decode_attn", "lrkv_decode_prepare", "lrkv_decode_partials", "lrkv_merge_partials",
     "lrkv_factor_page", "lrkv_paged_plan", "lrkv_project_workspace_bytes", "lrkv_latent_project",
-    "lrkv_output_project", "lrkv_probe_stream_read",
+    "lrkv_output_project", "lrkv_probe_stream_read", "lrkv_prefill_workspace_bytes", "lrkv_prefill_attn",
 )
 
 c_i32 = ctypes.c_int32
@@ -104,6 +104,11 @@ def lib() -> ctypes.CDLL:
         L.lrkv_output_project.restype = c_i32
         L.lrkv_probe_stream_read.argtypes = [c_vp, ctypes.c_size_t, c_vp, c_i32, c_vp]
         L.lrkv_probe_stream_read.restype = c_i32
+        L.lrkv_prefill_workspace_bytes.argtypes = [ctypes.POINTER(LatentCacheDesc), c_i32, c_i32]
+        L.lrkv_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.lrkv_prefill_attn.argtypes = [ctypes.POINTER(LatentCacheDesc), c_vp, c_vp, c_vp, c_i32, c_i32,
+                                        ctypes.c_float, c_vp, c_vp, ctypes.c_size_t, c_vp]
+        L.lrkv_prefill_attn.restype = c_i32
         _lib = L
     return _lib
 

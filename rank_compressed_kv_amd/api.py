@@ -227,6 +227,32 @@ class LatentCache:
         decode_attn(mode, self.desc, q, bk, q_pos, sm_scale, out, workspace, self.max_len, n_split, stream)
         return out
 
+    def prefill_workspace(self, m_tokens: int) -> torch.Tensor:
+        n = int(L.lib().lrkv_prefill_workspace_bytes(ctypes.byref(self.desc), m_tokens, self.max_len))
+        if n == 0:
+            raise LrkvError(L.LRKV_ERR_INVALID_ARG, "lrkv_prefill_workspace_bytes")
+        return torch.empty(n, dtype=torch.uint8, device=self.hk.device)
+
+    def prefill_attn(self, q: torch.Tensor, bk: torch.Tensor, p0: torch.Tensor, sm_scale: float = 0.0,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+        """Causal attention of a chunk of m new tokens (already appended at positions
+        p0[b] .. p0[b] + m - 1): q float32 [B][m][Hq][d_h], bk float16 [U][r][s*d_h],
+        p0 int32 [B] -> float32 [B][m][Hq][r]."""
+        m = q.shape[1]
+        _need(q, torch.float32, (self.B, m, self.Hq, self.dh), "q")
+        _need(bk, torch.float16, (self.U, self.r, self.s * self.dh), "bk")
+        _need(p0, torch.int32, (self.B,), "p0")
+        if out is None:
+            out = torch.empty((self.B, m, self.Hq, self.r), dtype=torch.float32, device=q.device)
+        _need(out, torch.float32, (self.B, m, self.Hq, self.r), "out")
+        if workspace is None:
+            workspace = self.prefill_workspace(m)
+        L.check(L.lib().lrkv_prefill_attn(ctypes.byref(self.desc), _p(q), _p(bk), _p(p0), m, self.max_len,
+                                          float(sm_scale), _p(out), _p(workspace), _ws(workspace),
+                                          _stream(stream)), "lrkv_prefill_attn")
+        return out
+
 
 class PagedCache:
     """Device buffers of a PuzzleKV-style hybrid cache (layouts in include/lrkv.h)."""

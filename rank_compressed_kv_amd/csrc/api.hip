@@ -348,6 +348,39 @@ int32_t lrkv_output_project(const float* o, int32_t batch, int32_t q_heads, int3
     return launch_skinny(o, (const half_t*)w_t, y, batch, d_model, K, workspace, p, (hipStream_t)stream);
 }
 
+// prefill: fp16 latents, rank 256, head_dim 128; host_max_len bounds p0[b] + m_tokens
+static int32_t check_prefill(const lrkv_latent_cache* c, int32_t m_tokens, int32_t host_max_len) {
+    int32_t rc = check_latent(c);
+    if (rc != LRKV_OK) return rc;
+    if (m_tokens < 1 || host_max_len < 1 || host_max_len > c->capacity) return LRKV_ERR_INVALID_ARG;
+    if ((long)c->batch * m_tokens * c->units * c->kv_per_unit * c->q_per_kv * c->head_dim >= (1L << 31))
+        return LRKV_ERR_INVALID_ARG;
+    if (c->fmt != LRKV_FMT_FP16 || c->rank != 256 || c->head_dim != 128) return LRKV_ERR_UNSUPPORTED;
+    return LRKV_OK;
+}
+
+size_t lrkv_prefill_workspace_bytes(const lrkv_latent_cache* c, int32_t m_tokens, int32_t host_max_len) {
+    if (check_prefill(c, m_tokens, host_max_len) != LRKV_OK) return 0;
+    const int Hq = c->units * c->kv_per_unit * c->q_per_kv;
+    return prefill_workspace_bytes(c->batch, m_tokens, Hq, c->head_dim, (host_max_len + kTile - 1) / kTile);
+}
+
+int32_t lrkv_prefill_attn(const lrkv_latent_cache* c, const float* q, const void* bk, const int32_t* p0,
+                          int32_t m_tokens, int32_t host_max_len, float sm_scale, float* out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+    int32_t rc = check_prefill(c, m_tokens, host_max_len);
+    if (rc != LRKV_OK) return rc;
+    if (!q || !bk || !p0 || !out || !aligned16(out) || !aligned16(q)) return LRKV_ERR_INVALID_ARG;
+    if (!isfinite(sm_scale)) return LRKV_ERR_INVALID_ARG;
+    const int Hq = c->units * c->kv_per_unit * c->q_per_kv;
+    const int n_tiles = (host_max_len + kTile - 1) / kTile;
+    if (!workspace || ws_bytes < prefill_workspace_bytes(c->batch, m_tokens, Hq, c->head_dim, n_tiles))
+        return LRKV_ERR_WORKSPACE;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
+    return launch_prefill(c, q, (const half_t*)bk, p0, m_tokens, n_tiles, scale, out, workspace,
+                          (hipStream_t)stream);
+}
+
 int32_t lrkv_probe_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* stream) {
     if (!buf || !out || bytes == 0 || (bytes % 16) || (((uintptr_t)buf) & 15) || blocks < 1 || blocks > 65535)
         return LRKV_ERR_INVALID_ARG;

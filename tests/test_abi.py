@@ -205,3 +205,24 @@ def test_projection_validation(lib):
     assert lib.lrkv_output_project(ok, 4, 32, 256, None, 4096, ok, ok, need, None) == L.LRKV_ERR_INVALID_ARG
     assert lib.lrkv_output_project(ok, 4, 32, 256, ok, 4095, ok, ok, need, None) == L.LRKV_ERR_UNSUPPORTED
     assert lib.lrkv_output_project(ok, 4, 32, 256, ok, 4096, ok, ok, need - 4, None) == L.LRKV_ERR_WORKSPACE
+
+
+def test_prefill_validation(lib):
+    d = _latent()
+    ok = ctypes.c_void_p(FAKE)
+    need = lib.lrkv_prefill_workspace_bytes(ctypes.byref(d), 512, 4096)
+    assert need >= 512 * 32 * 128 * 4
+    assert lib.lrkv_prefill_workspace_bytes(ctypes.byref(d), 0, 4096) == 0
+    assert lib.lrkv_prefill_workspace_bytes(ctypes.byref(d), 512, 4097) == 0        # beyond capacity
+    i4 = _latent(fmt=1, sk=FAKE, sv=FAKE)
+    assert lib.lrkv_prefill_workspace_bytes(ctypes.byref(i4), 512, 4096) == 0       # int4 latents
+    call = lambda desc, q=ok, m=512, hml=4096, ws=need, out=ok: lib.lrkv_prefill_attn(
+        ctypes.byref(desc), q, ok, ok, m, hml, 0.0, out, ok, ws, None)
+    assert call(d, q=None) == L.LRKV_ERR_INVALID_ARG
+    assert call(d, out=ctypes.c_void_p(FAKE + 4)) == L.LRKV_ERR_INVALID_ARG
+    assert call(d, m=0) == L.LRKV_ERR_INVALID_ARG
+    assert call(d, hml=4097) == L.LRKV_ERR_INVALID_ARG
+    assert call(d, ws=need - 1) == L.LRKV_ERR_WORKSPACE
+    assert call(i4) == L.LRKV_ERR_UNSUPPORTED
+    assert call(_latent(rank=128)) == L.LRKV_ERR_UNSUPPORTED
+    assert call(_latent(head_dim=64)) == L.LRKV_ERR_UNSUPPORTED
