@@ -166,6 +166,32 @@ def measure_rows(torch, lrkv, dev, iters: int = 20) -> dict:
         rows[f"output_project_B{nb}"] = _row(ms, w_t.numel() * 2, 2 * nb * w_t.numel())
     del a_t, w_t, x, o, h, y, wsl, wso
 
+    # chunked prefill on the RoPE path: Llama-2-7B layer, a 512-token chunk appended
+    # at position 65024 attends causally over the 64K-token latent cache. Algorithmic
+    # work: the reconstruction once per (token, head) plus scores and values per
+    # (query, visible token); the kernel redoes the reconstruction per 64-query block
+    # and forms scores from fp16 hi + lo parts (more MFMA work than counted)
+    g.manual_seed(7)
+    Tp, Mp = 65536, 512
+    c = lrkv.LatentCache(1, U, S, GQ, DH, R, Tp, lrkv.FMT_FP16, THETA, device=dev)
+    sq = torch.exp(-torch.arange(R, device=dev, dtype=torch.float32) / (2 * TAU))
+    for t0 in range(0, Tp, 16384):
+        c.append(torch.randn((1, U, 16384, R), generator=g, device=dev) * sq,
+                 torch.randn((1, U, 16384, R), generator=g, device=dev) * sq)
+    qp = torch.randn((1, Mp, U * S * GQ, DH), generator=g, device=dev)
+    bkp = (torch.randn((U, R, S * DH), generator=g, device=dev) / 16).half()
+    p0 = torch.full((1,), Tp - Mp, dtype=torch.int32, device=dev)
+    wsp = c.prefill_workspace(Mp)
+    outp = torch.empty((1, Mp, U * S * GQ, R), dtype=torch.float32, device=dev)
+    ms = _time(torch, lambda: c.prefill_attn(qp, bkp, p0, out=outp, workspace=wsp), 10)
+    heads = U * S * GQ
+    vis = float(sum(Tp - Mp + m + 1 for m in range(Mp)))
+    flops_p = 2.0 * R * DH * Tp * heads + 2.0 * (DH + R) * vis * heads
+    rows["prefill_chunk512_T65536"] = _row(ms, U * Tp * 2 * R * 2, flops_p)
+    rows["prefill_chunk512_T65536"]["frac_mfma_peak"] = round(flops_p / (float(np.median(ms)) * 1e-3) / 1e12
+                                                             / MFMA_F16_PEAK_TFLOPS, 4)
+    del c, qp, bkp, p0, wsp, outp
+
     # RoPE path over Hadamard-rotated int4 latents: Llama-3-8B GQA, rank 64 per KV head
     g.manual_seed(4)
     B4, T4, H4, G4, R4 = 4, 65536, 8, 4, 64

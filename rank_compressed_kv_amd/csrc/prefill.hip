@@ -190,12 +190,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // (cos, sin) of the tile start for the lane's frequencies: loaded one tile ahead,
+    // after the current tile's rotation, so the wait at the tile top covers them
+    float2 st[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st[i] = a.ang[freq(i)];
     for (int t = 0; t < n_t; ++t) {
         const int t0 = 32 * t;
-        float2 st[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)t * (DH / 2) + freq(i)];
-        wait_vmem();
+        // vmcnt(0) as a builtin: the compiler sees it, so it inserts no later wait for
+        // its own loads (which would also stall on the next tile's loads below)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();                      // tile t in LDS; tile t-1 fully consumed
         if (t + 1 < n_t) issue(t + 1);
 
@@ -231,23 +235,36 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
                 *reinterpret_cast<half4*>(&krot[1][o_hi]) = half4{hl[0], hl[1], hl[2], hl[3]};
             }
         }
+        if (t + 1 < n_t) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)(t + 1) * (DH / 2) + freq(i)];
+        }
         __syncthreads();                      // K of tile t complete
 
         // ---- S^T [token][row]: block mb row m is token 8 (m/4) + 4 mb + m % 4
-        floatx4 S[2];
+        // four independent accumulation chains: (hi x hi) and (hi x lo + lo x hi) per block
+        floatx4 S[2], S2[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int tk = 8 * (c >> 2) + 4 * mb + (c & 3);
-            S[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < 2; ++mb) S[mb] = S2[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 4; ++ks) {
+            half8 kh[2], kl[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int tk = 8 * (c >> 2) + 4 * mb + (c & 3);
                 const int off = tk * DH + 8 * ((4 * ks + g) ^ (tk & 15));
-                const half8 kh = lds8(&krot[0][off]), kl = lds8(&krot[1][off]);
-                S[mb] = mfma16(kh, qh[ks], S[mb]);
-                S[mb] = mfma16(kh, ql[ks], S[mb]);
-                S[mb] = mfma16(kl, qh[ks], S[mb]);
+                kh[mb] = lds8(&krot[0][off]);
+                kl[mb] = lds8(&krot[1][off]);
             }
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) S[mb] = mfma16(kh[mb], qh[ks], S[mb]);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) S2[mb] = mfma16(kh[mb], ql[ks], S2[mb]);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) S2[mb] = mfma16(kl[mb], qh[ks], S2[mb]);
         }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) S[mb] += S2[mb];
         // lane (c, g): row c at tokens t0 + 8 g + j, j = 4 mb + i
         float sv[8];
 #pragma unroll
