@@ -361,8 +361,8 @@ static int32_t check_prefill(const lrkv_latent_cache* c, int32_t m_tokens, int32
 
 size_t lrkv_prefill_workspace_bytes(const lrkv_latent_cache* c, int32_t m_tokens, int32_t host_max_len) {
     if (check_prefill(c, m_tokens, host_max_len) != LRKV_OK) return 0;
-    const int Hq = c->units * c->kv_per_unit * c->q_per_kv;
-    return prefill_workspace_bytes(c->batch, m_tokens, Hq, c->head_dim, (host_max_len + kTile - 1) / kTile);
+    return prefill_workspace_bytes(c->batch, c->units, c->kv_per_unit, c->q_per_kv, m_tokens, c->head_dim, c->rank,
+                                   (host_max_len + kTile - 1) / kTile);
 }
 
 int32_t lrkv_prefill_attn(const lrkv_latent_cache* c, const float* q, const void* bk, const int32_t* p0,
@@ -374,7 +374,8 @@ int32_t lrkv_prefill_attn(const lrkv_latent_cache* c, const float* q, const void
     if (!isfinite(sm_scale)) return LRKV_ERR_INVALID_ARG;
     const int Hq = c->units * c->kv_per_unit * c->q_per_kv;
     const int n_tiles = (host_max_len + kTile - 1) / kTile;
-    if (!workspace || ws_bytes < prefill_workspace_bytes(c->batch, m_tokens, Hq, c->head_dim, n_tiles))
+    if (!workspace || ws_bytes < prefill_workspace_bytes(c->batch, c->units, c->kv_per_unit, c->q_per_kv, m_tokens,
+                                                          c->head_dim, c->rank, n_tiles))
         return LRKV_ERR_WORKSPACE;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
     return launch_prefill(c, q, (const half_t*)bk, p0, m_tokens, n_tiles, scale, out, workspace,

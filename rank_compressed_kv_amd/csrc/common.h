@@ -139,7 +139,7 @@ SkinnyPlan skinny_plan(int M, int N, int K);
 int32_t launch_skinny(const float* X, const half_t* Wt, float* C, int M, int N, int K, void* ws,
                       const SkinnyPlan& p, hipStream_t st);
 int32_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t st);
-size_t prefill_workspace_bytes(int B, int M, int Hq, int DH, int n_tiles);
+size_t prefill_workspace_bytes(int B, int U, int s, int gq, int M, int DH, int R, int n_tiles);
 int32_t launch_prefill(const lrkv_latent_cache* c, const float* q, const half_t* bk, const int32_t* p0, int M,
                        int n_tiles, float sm_scale, float* out, void* ws, hipStream_t st);
 int32_t launch_factor_page(const lrkv_paged_cache* c, const int32_t* pages, int n_pages,

@@ -87,23 +87,44 @@ struct PrefillArgs {
     const int32_t* lens;
     const float* qr;      // [B][M][Hq][DH] rotated, scaled
     const float2* ang;    // [n_tiles + 32][DH/2]
-    float* out;           // [B][M][Hq][R]
-    int B, U, s, gq, M, cap, n_tiles, n_qb;
+    float* part;          // [B][M][Hq][n_split][R + 2]: (max, sum, unnormalised output)
+    int B, U, s, gq, M, cap, n_tiles, n_qb, n_split, tps;
 };
 
 __device__ __forceinline__ half8 lds8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
 
+// max / sum over the four lane groups of a column
+__device__ __forceinline__ float col_max(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    v = fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    v = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+    return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// One workgroup per (sequence, unit, KV head of the unit, block of 128 query rows,
+// key split): wave w owns rows 32 w .. 32 w + 31 as two 16-row blocks, which share
+// every K and V fragment the wave reads; the key tiles of split sp are
+// [sp tps, (sp + 1) tps) up to the block's causal end.
 template <int R>
 __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
-    constexpr int DH = 128, KS = R / 16, NDB = R / 16;
+    constexpr int DH = 128, KS = R / 16, NDB = R / 16, NRB = 2;
     static_assert(R == 256, "prefill kernel covers rank 256");
     __shared__ __attribute__((aligned(1024))) half_t htile[2][32 * R];    // H^k [token][rank], chunks swizzled
     __shared__ __attribute__((aligned(1024))) half_t vtile[2][R * 32];    // H^v [rank][token], chunks swizzled
     __shared__ __attribute__((aligned(16))) half_t krot[2][32 * DH];      // K hi, lo [token][dim], chunks swizzled
+    __shared__ float2 tokb[32][DH / 2];                                   // (cos, sin)(tau theta_f), tau < 32
 
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int c = l & 15, g = l >> 4;
     int blk = blockIdx.x;
+    const int sp = blk % a.n_split;
+    blk /= a.n_split;
     const int qb = blk % a.n_qb;
     blk /= a.n_qb;
     const int w = blk % a.s;
@@ -113,18 +134,39 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
     const int Hq = a.U * a.s * a.gq;
     const int len = min(a.lens[b], a.cap);
     const int rows = a.M * a.gq;
-    const int row0 = qb * 64;
+    const int row0 = qb * 128;
     if (len <= 0 || row0 >= rows) return;
 
-    // this lane's query row (column c of the wave's score tiles)
-    const int rho = row0 + 16 * wv + c;
-    const bool row_ok = rho < rows;
-    const int m_row = row_ok ? rho / a.gq : 0;
-    const int j_row = (u * a.s + w) * a.gq + (row_ok ? rho % a.gq : 0);
-    const int pos = row_ok ? qpos(a.p0, a.lens, b, m_row) : -1;
-    // the block's last position (rows ascend with the chunk token)
-    const int m_last = (min(rows, row0 + 64) - 1) / a.gq;
+    // the lane's query rows (column c of the wave's two score blocks)
+    int m_row[NRB], j_row[NRB], pos[NRB];
+    bool row_ok[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const int rho = row0 + 32 * wv + 16 * rb + c;
+        row_ok[rb] = rho < rows;
+        m_row[rb] = row_ok[rb] ? rho / a.gq : 0;
+        j_row[rb] = (u * a.s + w) * a.gq + (row_ok[rb] ? rho % a.gq : 0);
+        pos[rb] = row_ok[rb] ? qpos(a.p0, a.lens, b, m_row[rb]) : -1;
+    }
+    const int m_last = (min(rows, row0 + 128) - 1) / a.gq;
     const int n_t = min(a.n_tiles, qpos(a.p0, a.lens, b, m_last) / 32 + 1);
+    const int t_beg = sp * a.tps, t_end = min(n_t, t_beg + a.tps);
+
+    auto part_of = [&](int rb) {
+        return a.part + (((long)(b * a.M + m_row[rb]) * Hq + j_row[rb]) * a.n_split + sp) * (R + 2);
+    };
+    if (t_beg >= t_end) {
+        // an empty split: (max, sum, output) = (-inf, 0, 0) for every row
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            if (row_ok[rb] && g == 0) {
+                float* pp = part_of(rb);
+                pp[0] = -INFINITY;
+                pp[1] = 0.0f;
+                for (int d = 0; d < R; ++d) pp[2 + d] = 0.0f;
+            }
+        return;
+    }
 
     const long bu = (long)b * a.U + u;
     const half_t* hk = a.hk + bu * a.cap * R;
@@ -144,7 +186,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
             buf_dma16(vr, vx + 1024u * n, vtile[t & 1] + (4 * wv + n) * 512);
         }
     };
-    issue(0);
+    issue(t_beg);
 
     // B^T fragments: A operand of K^T = B^T H^T. Row m of the wave's 32 dims is
     // dim 16 wv + m (m < 16) or 64 + 16 wv + m - 16; K step ks covers ranks
@@ -159,49 +201,49 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) bf[ks][e] = col[(long)(16 * ks + 8 * (l >> 5) + e) * (a.s * DH)];
     }
-    // queries of the lane's row, dims 32 ks + 8 g + e, as fp16 hi + lo
-    half8 qh[4], ql[4];
-    {
-        const float* qs = a.qr + ((long)(b * a.M + m_row) * Hq + j_row) * DH;
+    // queries of the lane's rows, dims 32 ks + 8 g + e, as fp16 hi + lo
+    half8 qh[NRB][4], ql[NRB][4];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const float* qs = a.qr + ((long)(b * a.M + m_row[rb]) * Hq + j_row[rb]) * DH;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = row_ok ? qs[32 * ks + 8 * g + e] : 0.0f;
-                qh[ks][e] = (half_t)v;
-                ql[ks][e] = (half_t)(v - (float)qh[ks][e]);
+                const float v = row_ok[rb] ? qs[32 * ks + 8 * g + e] : 0.0f;
+                qh[rb][ks][e] = (half_t)v;
+                ql[rb][ks][e] = (half_t)(v - (float)qh[rb][ks][e]);
             }
     }
-    // in-tile offsets (cos, sin)(tau theta_f) of the lane's token tau = l % 32 and
-    // its eight frequencies f_i = 16 wv + 8 (i / 4) + 4 (l / 32) + i % 4
-    float2 tok[8];
+    // in-tile offsets (cos, sin)(tau theta_f) to LDS; the lane's token is tau = l % 32
+    // and its eight frequencies f_i = 16 wv + 8 (i / 4) + 4 (l / 32) + i % 4
+    for (int e = tid; e < 32 * (DH / 2); e += 256) (&tokb[0][0])[e] = a.ang[(long)a.n_tiles * (DH / 2) + e];
     auto freq = [&](int i) { return 16 * wv + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3); };
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tok[i] = a.ang[(long)(a.n_tiles + (l & 31)) * (DH / 2) + freq(i)];
-
     // key fragment of the reconstruction (B operand): token l % 32, ranks 16 ks + 8 (l/32)
-    int koff[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) koff[q] = (l & 31) * R + 8 * ((2 * q + (l >> 5)) ^ (l & 15));
+    auto koff = [&](int ks) { return (l & 31) * R + 8 * ((2 * (ks & 7) + (l >> 5)) ^ (l & 15)) + 128 * (ks >> 3); };
     const int vro = 8 * (4 * (l & 15) + ((l >> 4) ^ vswz(l & 15)));
 
-    float m_run = -INFINITY, l_lane = 0.0f;
-    floatx4 o[NDB];
+    float m_run[NRB], l_lane[NRB];
+    floatx4 o[NRB][NDB];
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < NRB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_lane[rb] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[rb][d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    // (cos, sin) of the tile start for the lane's frequencies: loaded one tile ahead,
-    // after the current tile's rotation, so the wait at the tile top covers them
+    // (cos, sin) of the tile start for the lane's frequencies: loaded one tile ahead
     float2 st[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st[i] = a.ang[freq(i)];
-    for (int t = 0; t < n_t; ++t) {
+    for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)t_beg * (DH / 2) + freq(i)];
+    for (int t = t_beg; t < t_end; ++t) {
         const int t0 = 32 * t;
         // vmcnt(0) as a builtin: the compiler sees it, so it inserts no later wait for
         // its own loads (which would also stall on the next tile's loads below)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();                      // tile t in LDS; tile t-1 fully consumed
-        if (t + 1 < n_t) issue(t + 1);
+        if (t + 1 < t_end) issue(t + 1);
 
         // ---- K^T for the wave's 32 dims, RoPE, K hi / lo to LDS
         {
@@ -209,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
             floatx16 acc = floatx16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                acc = mfma32(bf[ks], lds8(ht + koff[ks & 7] + 128 * (ks >> 3)), acc);
+                acc = mfma32(bf[ks], lds8(ht + koff(ks)), acc);
             const int tl = l & 31;
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
@@ -217,8 +259,9 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * gi + e;
-                    const float cc = st[i].x * tok[i].x - st[i].y * tok[i].y;
-                    const float ss = st[i].x * tok[i].y + st[i].y * tok[i].x;
+                    const float2 tk = tokb[tl][freq(i)];
+                    const float cc = st[i].x * tk.x - st[i].y * tk.y;
+                    const float ss = st[i].x * tk.y + st[i].y * tk.x;
                     const float lo = acc[i], hi = acc[i + 8];
                     const float lo2 = lo * cc - hi * ss, hi2 = hi * cc + lo * ss;
                     lh[e] = (half_t)lo2;
@@ -235,17 +278,19 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
                 *reinterpret_cast<half4*>(&krot[1][o_hi]) = half4{hl[0], hl[1], hl[2], hl[3]};
             }
         }
-        if (t + 1 < n_t) {
+        if (t + 1 < t_end) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)(t + 1) * (DH / 2) + freq(i)];
         }
         __syncthreads();                      // K of tile t complete
 
-        // ---- S^T [token][row]: block mb row m is token 8 (m/4) + 4 mb + m % 4
-        // four independent accumulation chains: (hi x hi) and (hi x lo + lo x hi) per block
-        floatx4 S[2], S2[2];
+        // ---- S^T [token][row] for both row blocks: block mb row m is token
+        // 8 (m/4) + 4 mb + m % 4; hi x hi + hi x lo + lo x hi, four chains
+        floatx4 S[NRB][2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) S[mb] = S2[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) S[rb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             half8 kh[2], kl[2];
@@ -257,45 +302,45 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
                 kl[mb] = lds8(&krot[1][off]);
             }
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) S[mb] = mfma16(kh[mb], qh[ks], S[mb]);
+            for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) S2[mb] = mfma16(kh[mb], ql[ks], S2[mb]);
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) S2[mb] = mfma16(kl[mb], qh[ks], S2[mb]);
+                for (int mb = 0; mb < 2; ++mb) {
+                    S[rb][mb] = mfma16(kh[mb], qh[rb][ks], S[rb][mb]);
+                    S[rb][mb] = mfma16(kh[mb], ql[rb][ks], S[rb][mb]);
+                    S[rb][mb] = mfma16(kl[mb], qh[rb][ks], S[rb][mb]);
+                }
         }
+
+        // ---- causal mask and online softmax per row block; lane (c, g): row c at
+        // tokens t0 + 8 g + jj, jj = 4 mb + i
+        half8 pb[NRB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) S[mb] += S2[mb];
-        // lane (c, g): row c at tokens t0 + 8 g + j, j = 4 mb + i
-        float sv[8];
+        for (int rb = 0; rb < NRB; ++rb) {
+            float sv[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int tkn = t0 + 8 * g + jj;
-            sv[jj] = tkn <= pos ? S[jj >> 2][jj & 3] : -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        {
-            auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx), false, false);
-            mx = fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
-            r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx), false, false);
-            mx = fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
-        }
-        const float mn = fmaxf(m_run, mx);
-        if (__builtin_amdgcn_ballot_w64(mn > m_run)) {
-            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
-            l_lane *= alpha;
+            for (int jj = 0; jj < 8; ++jj) {
+                const float v = S[rb][jj >> 2][jj & 3];
+                sv[jj] = t0 + 8 * g + jj <= pos[rb] ? v : -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mx = col_max(mx);
+            const float mn = fmaxf(m_run[rb], mx);
+            if (__builtin_amdgcn_ballot_w64(mn > m_run[rb])) {
+                const float alpha = m_run[rb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
+                l_lane[rb] *= alpha;
 #pragma unroll
-            for (int d = 0; d < NDB; ++d) o[d] *= alpha;
-        }
-        m_run = mn;
-        half8 pb;
-        float psum = 0.0f;
+                for (int d = 0; d < NDB; ++d) o[rb][d] *= alpha;
+            }
+            m_run[rb] = mn;
+            float psum = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const float pv = sv[jj] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[jj] - mn);
-            psum += pv;
-            pb[jj] = (half_t)pv;
+            for (int jj = 0; jj < 8; ++jj) {
+                const float pv = sv[jj] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[jj] - mn);
+                psum += pv;
+                pb[rb][jj] = (half_t)pv;
+            }
+            l_lane[rb] += psum;
         }
-        l_lane += psum;
 
         // ---- O^T [dim][row] += V^T P^T (tokens past the sequence end zeroed)
         {
@@ -310,49 +355,71 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
                     for (int e = 0; e < 8; ++e)
                         if (first + e >= len) va[e] = (half_t)0.0f;
                 }
-                o[d] = mfma16(va, pb, o[d]);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) o[rb][d] = mfma16(va, pb[rb], o[rb][d]);
             }
         }
     }
 
-    // lane (c, g) holds dims 16 d + 4 g + i of row c
-    float lsum = l_lane;
-    {
-        auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, lsum), __builtin_bit_cast(int, lsum), false, false);
-        lsum = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
-        r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, lsum), __builtin_bit_cast(int, lsum), false, false);
-        lsum = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
-    }
-    if (row_ok) {
-        const float inv = 1.0f / lsum;
-        float* op = a.out + ((long)(b * a.M + m_row) * Hq + j_row) * R + 4 * g;
+    // the split's state per row: lane (c, g) holds dims 16 d + 4 g + i of row c
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
-            *reinterpret_cast<float4*>(op + 16 * d) = make_float4(o[d][0] * inv, o[d][1] * inv, o[d][2] * inv, o[d][3] * inv);
+    for (int rb = 0; rb < NRB; ++rb) {
+        const float lsum = col_sum(l_lane[rb]);
+        if (row_ok[rb]) {
+            float* pp = part_of(rb);
+            if (g == 0) {
+                pp[0] = m_run[rb];
+                pp[1] = lsum;
+            }
+#pragma unroll
+            for (int d = 0; d < NDB; ++d)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pp[2 + 16 * d + 4 * g + i] = o[rb][d][i];
+        }
     }
 }
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int B, int M, int Hq, int DH, int n_tiles) {
-    return align_up((size_t)(n_tiles + 32) * (DH / 2) * sizeof(float2), 256) +
-           align_up((size_t)B * M * Hq * DH * sizeof(float), 256);
+// Key splits: enough workgroups for about one per compute unit, at least one tile each.
+static int prefill_splits(int B, int U, int s, int n_qb, int n_tiles) {
+    const long groups = (long)B * U * s * n_qb;
+    long n = (256 + groups - 1) / groups;
+    if (n > n_tiles) n = n_tiles;
+    if (n > 256) n = 256;
+    return n < 1 ? 1 : (int)n;
 }
+
+size_t prefill_workspace_bytes(int B, int U, int s, int gq, int M, int DH, int R, int n_tiles) {
+    const int Hq = U * s * gq, n_qb = (M * gq + 127) / 128;
+    const int n_split = prefill_splits(B, U, s, n_qb, n_tiles);
+    return align_up((size_t)(n_tiles + 32) * (DH / 2) * sizeof(float2), 256) +
+           align_up((size_t)B * M * Hq * DH * sizeof(float), 256) +
+           align_up((size_t)B * M * Hq * n_split * (R + 2) * sizeof(float), 256);
+}
+
+void launch_merge(const float* part, float* out, int BH, int n_split, int D, hipStream_t st);
 
 int32_t launch_prefill(const lrkv_latent_cache* c, const float* q, const half_t* bk, const int32_t* p0, int M,
                        int n_tiles, float sm_scale, float* out, void* ws, hipStream_t st) {
-    const int Hq = c->units * c->kv_per_unit * c->q_per_kv, DH = c->head_dim;
+    const int Hq = c->units * c->kv_per_unit * c->q_per_kv, DH = c->head_dim, R = c->rank;
+    const int n_qb = (M * c->q_per_kv + 127) / 128;
+    const int n_split = prefill_splits(c->batch, c->units, c->kv_per_unit, n_qb, n_tiles);
+    const int tps = (n_tiles + n_split - 1) / n_split;
+    const size_t ang_bytes = align_up((size_t)(n_tiles + 32) * (DH / 2) * sizeof(float2), 256);
+    const size_t q_bytes = align_up((size_t)c->batch * M * Hq * DH * sizeof(float), 256);
     float2* ang = (float2*)ws;
-    float* qr = (float*)((char*)ws + align_up((size_t)(n_tiles + 32) * (DH / 2) * sizeof(float2), 256));
+    float* qr = (float*)((char*)ws + ang_bytes);
+    float* part = (float*)((char*)ws + ang_bytes + q_bytes);
     PrefillPrepArgs pa{q, p0, c->lens, qr, ang, c->batch, M, Hq, DH, n_tiles, (double)c->rope_theta,
                        sm_scale * kLog2e};
     const long n_prep = (long)(n_tiles + 32) * (DH / 2) + (long)c->batch * M * Hq * (DH / 2);
     hipLaunchKernelGGL(prefill_prep, dim3((unsigned)((n_prep + 255) / 256)), dim3(256), 0, st, pa);
-    const int n_qb = (M * c->q_per_kv + 63) / 64;
-    PrefillArgs a{(const half_t*)c->hk, (const half_t*)c->hv, bk, p0, c->lens, qr, ang, out,
-                  c->batch, c->units, c->kv_per_unit, c->q_per_kv, M, c->capacity, n_tiles, n_qb};
-    const long blocks = (long)c->batch * c->units * c->kv_per_unit * n_qb;
+    PrefillArgs a{(const half_t*)c->hk, (const half_t*)c->hv, bk, p0, c->lens, qr, ang, part,
+                  c->batch, c->units, c->kv_per_unit, c->q_per_kv, M, c->capacity, n_tiles, n_qb, n_split, tps};
+    const long blocks = (long)c->batch * c->units * c->kv_per_unit * n_qb * n_split;
     hipLaunchKernelGGL(prefill_attn<256>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    launch_merge(part, out, c->batch * M * Hq, n_split, R, st);
     return last_launch_status();
 }
 
