@@ -20,7 +20,9 @@
 // contiguous run of the contraction index. Heads c >= G are zero columns.
 // Query and u = q R_K^T enter the MFMA as fp16 hi + lo pairs (u's magnitude
 // grows with the factor scale; one fp16 rounding of it would cost ~1e-3 of the
-// output), p and w once rounded to fp16.
+// output), p and w once rounded to fp16. With int4 factors the key-side factors
+// (R_K, L_K) also enter as exact hi + lo pairs of code x scale, since a rounded
+// key factor moves the scores; the value-side factors are rounded once.
 //
 // Factored pages stream through three register buffers (two pages in flight
 // while one is computed); dense pages (sink and window, a handful per
@@ -70,6 +72,35 @@ __device__ __forceinline__ half4 decode4(uint32_t w16, uint32_t scale_bits) {
 }
 // the order decode4 yields: element e is code pi4(e)
 __host__ __device__ constexpr int pi4(int e) { return e == 1 ? 2 : e == 2 ? 1 : e; }
+
+// Key-side factors as exact fp16 pairs: code x scale has at most 14 significant
+// bits, so hi = fp16(code x scale) and lo = fma(code, scale, -hi) (one rounding of
+// an exactly representable residual) give hi + lo = code x scale.
+__device__ __forceinline__ void decode4_hl(uint32_t w16, uint32_t scale_bits, half4& hi, half4& lo) {
+    const uint32_t x = (w16 ^ 0x8888u), y = __builtin_amdgcn_perm(0u, x, 0x0C010C00u);
+    const uint32_t magic = 0x64006400u;
+    const half2_t lo_off = {-1032.0f16, -1032.0f16};
+    const half2_t hi_mul = {0.0625f16, 0.0625f16}, hi_off = {-72.0f16, -72.0f16};
+    const half2_t s2 = __builtin_bit_cast(half2_t, scale_bits * 0x00010001u);
+    const half2_t ca = __builtin_bit_cast(half2_t, and_or(y, 0x000F000Fu, magic)) + lo_off;
+    const half2_t cb = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(y, 0x00F000F0u, magic)), hi_mul, hi_off);
+    const half2_t ha = ca * s2, hb = cb * s2;
+    const half2_t la = __builtin_elementwise_fma(ca, s2, -ha), lb = __builtin_elementwise_fma(cb, s2, -hb);
+    hi = half4{ha[0], ha[1], hb[0], hb[1]};
+    lo = half4{la[0], la[1], lb[0], lb[1]};
+}
+__device__ __forceinline__ void dequant_keys_hl(uint32_t w, uint32_t sc, uint32_t magic, half8& hi, half8& lo) {
+    half2_t r[4], h[4], e[4];
+    unpack_codes(w, magic, r);
+    const half2_t s2 = __builtin_bit_cast(half2_t, sc * 0x00010001u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = r[j] * s2;
+        e[j] = __builtin_elementwise_fma(r[j], s2, -h[j]);
+    }
+    hi = as_half8(h);
+    lo = as_half8(e);
+}
 
 // max / sum over the four lane groups (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float xg_max(float v) {
@@ -318,22 +349,28 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
     auto factored4 = [&](const FPage4& f, int ntok) __attribute__((always_inline)) {
         const uint32_t magic = 0x64006400u;
         const uint32_t rw[4] = {f.rk.x, f.rk.y, f.rk.z, f.rk.w};
-        floatx4 u = floatx4{0.f, 0.f, 0.f, 0.f};
+        // u = (R_K hi + lo)(q hi + lo) without the lo x lo term
+        floatx4 u = floatx4{0.f, 0.f, 0.f, 0.f}, u2 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const half8 ak = dequant_keys(rw[s], f.rks, magic);
-            u = mfma16(ak, qh[s], u);
-            u = mfma16(ak, ql[s], u);
+            half8 akh, akl;
+            dequant_keys_hl(rw[s], f.rks, magic, akh, akl);
+            u = mfma16(akh, qh[s], u);
+            u2 = mfma16(akh, ql[s], u2);
+            u2 = mfma16(akl, qh[s], u2);
         }
+        u += u2;
         // lane (c, g) holds U^T[4 g + i][c]; L_K fragments decode in rank order pi4
         half4 uh, ul;
         split4(floatx4{u[0], u[2], u[1], u[3]}, uh, ul);
         floatx4 S[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const half4 lk = decode4(f.lk[tb], f.lks[tb]);
-            S[tb] = mfma16k16(lk, uh, floatx4{0.f, 0.f, 0.f, 0.f});
-            S[tb] = mfma16k16(lk, ul, S[tb]);
+            half4 lkh, lkl;
+            decode4_hl(f.lk[tb], f.lks[tb], lkh, lkl);
+            S[tb] = mfma16k16(lkh, uh, floatx4{0.f, 0.f, 0.f, 0.f});
+            S[tb] = mfma16k16(lkh, ul, S[tb]);
+            S[tb] = mfma16k16(lkl, uh, S[tb]);
         }
         half4 pb[2];
         softmax(S, ntok, pb, true);

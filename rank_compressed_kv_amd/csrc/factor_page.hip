@@ -15,7 +15,10 @@
 //      sweep skips every pair or after max_sweeps.
 //   3. Eigenvalues sorted descending (ties: lower index first); L = the first r
 //      eigenvectors rounded to fp16, R = L^T X accumulated in fp32, stored fp16
-//      (value pages transposed: L^T and R^T, the layout the decode reads).
+//      (value pages transposed: L^T and R^T, the layout the decode reads). With
+//      int4 factors (PuzzleKV, per-factor INT4) L is quantised in groups of 32
+//      stored elements first and R = L_hat^T X is formed from the dequantised
+//      L_hat, then quantised likewise (value R^T in rank quads).
 // The page-table entries are switched to "factored" by a second kernel so that
 // the K and V waves of one page never race on them.
 #include "common.h"

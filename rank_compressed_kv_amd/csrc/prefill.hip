@@ -6,9 +6,10 @@
 //
 // With many queries per token the reconstruction is shared by all of them, so
 // it is done as a GEMM per 32-token key tile (no query-rotated basis): one
-// workgroup of 4 waves per (sequence, unit, KV head of the unit, block of 64
-// query rows), a query row being one (token, query head) pair of that KV head.
-// Per key tile:
+// workgroup of 4 waves per (sequence, unit, KV head of the unit, block of 128
+// query rows, key split), a query row being one (token, query head) pair of that
+// KV head; the splits' (max, sum, output) states are combined by the split-K
+// merge of the decode path. Per key tile:
 //   K^T [dim][token] = B^T H^T   32x32x16 MFMA, wave w owning dims
 //                                16 w .. 16 w + 15 and their RoPE partners
 //                                64 + 16 w .. (B^T fragments in registers), so a
@@ -16,7 +17,7 @@
 //   RoPE at each token's position in registers, (cos, sin) = tile start x
 //   in-tile offset (both fp64-reduced by the prepare kernel); K written to LDS
 //   as fp16 hi + lo;
-//   S^T [token][row] = K Q^T     16x16x32 MFMA, wave w owning 16 query rows,
+//   S^T [token][row] = K Q^T     16x16x32 MFMA, wave w owning 32 query rows,
 //                                rows of K permuted so that a lane's output is 8
 //                                consecutive tokens of one query row; hi x hi,
 //                                hi x lo, lo x hi;

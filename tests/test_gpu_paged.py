@@ -408,6 +408,28 @@ def test_int4_decode_loop_end_to_end():
     assert e_gpu <= 2 * e_oracle + TOL, (e_gpu, e_oracle)
 
 
+def test_hybrid_int4_sink_window_geometry():
+    """int4 factors with 2 sink and 3 window pages, unequal ranks (8 / 4): the page
+    table and dense slots follow the geometry, decode against the oracle."""
+    R = _R()
+    B, H, G, T, rk, rv = 2, 2, 4, 32 * 17 + 9, 8, 4
+    say(f"hybrid int4 sink/window: T={T} rk={rk} rv={rv}")
+    cache = R.PagedCache(B, H, G, 128, P, 2, 3, rk, rv, max_pages=(T + P - 1) // P + 1,
+                         factor_fmt=R.FMT_INT4_G32)
+    dense = synth.paged_dense(81, B, H, T, 128)
+    npg = (T + P - 1) // P
+    fk = synth.factored_pages(82, B * H * npg, P, 128, rk)
+    fv = synth.factored_pages(83, B * H * npg, P, 128, rv)
+    shp = lambda a, last: a.reshape((B, H, npg) + last).astype(np.float64)
+    Lk, Rk = shp(fk["L"], (P, rk)), shp(fk["R"], (rk, 128))
+    Lv, Rv = shp(fv["L"], (P, rv)), shp(fv["R"], (rv, 128))
+    Lk, Rk, Lv, Rv = _write_int4_cache(cache, dense["k"], dense["v"], Lk, Rk, Lv, Rv, T)
+    q = synth.queries(84, B, H * G, 128, 2.0)
+    got = cache.decode(to_dev(q)).cpu().numpy()
+    ref = opaged.hybrid_decode(q, [T] * B, dense["k"], dense["v"], Lk, Rk, Lv, Rv, P, 2, 3, G)
+    assert rel_l2(got, ref).max() <= TOL
+
+
 def test_hybrid_int4_split_independence():
     R = _R()
     B, H, G, T = 1, 2, 4, 32 * 40

@@ -113,3 +113,22 @@ def test_prefill_full_size_sampled():
         ref = oattn.palu_decode(hk, hv, bk16[u:u + 1].astype(np.float64), q[:, m, u * s * gq:(u + 1) * s * gq],
                                 [n], s, gq, DH, THETA)
         assert rel_l2(got[0, m, j], ref[0, j - u * s * gq]) <= TOL, (m, j)
+
+
+def test_prefill_without_rope():
+    """rope_theta = 0: plain reconstruct-and-attend (no rotation on either side)."""
+    import rank_compressed_kv_amd as Rk
+    B, U, s, gq, T0, M, cap = 1, 1, 4, 1, 200, 60, 288
+    say(f"prefill no RoPE: T0={T0} M={M}")
+    lay = synth.latent_layer(47, B, U, T0 + M, R, s * DH, 96.0)
+    c = Rk.LatentCache(B, U, s, gq, DH, R, cap, Rk.FMT_FP16, 0.0)
+    c.append(to_dev(lay["hk"].astype(np.float32)), to_dev(lay["hv"].astype(np.float32)))
+    bk16 = lay["Bk"].astype(np.float16)
+    Hq = U * s * gq
+    q = synth.queries(48, B * M, Hq, DH, 1.0).reshape(B, M, Hq, DH)
+    p0 = np.full(B, T0, np.int32)
+    got = c.prefill_attn(to_dev(q), to_dev(bk16), to_dev(p0)).cpu().numpy()
+    ref = oattn.palu_prefill(oattn.stored_fp16(lay["hk"]), oattn.stored_fp16(lay["hv"]),
+                             bk16.astype(np.float64), q, p0, s, gq, DH, 0.0)
+    err = rel_l2(got.reshape(B * M, Hq, R), ref.reshape(B * M, Hq, R))
+    assert err.max() <= TOL, err.max()
