@@ -26,7 +26,12 @@ __all__ = [
 
 
 def _p(t) -> ctypes.c_void_p | None:
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Raw pointer of a tensor handed to the C ABI, which reads dense row-major memory."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError(f"tensor of shape {tuple(t.shape)} is not contiguous (the C ABI reads row-major memory)")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream=None) -> ctypes.c_void_p:

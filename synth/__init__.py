@@ -104,7 +104,7 @@ def latent_layer(seed: int, batch: int, units: int, T: int, rank: int, width: in
         for _ in range(units):
             V = haar_orthonormal(rng, width, rank)          # width x rank
             mats.append((root[:, None] * V.T).astype(np.float16))
-        Bs[kind] = np.stack(mats)
+        Bs[kind] = np.ascontiguousarray(np.stack(mats))     # C order (V.T would leave it strided)
     hk = rng.standard_normal((batch, units, T, rank), dtype=np.float32)
     hk *= root.astype(np.float32)
     hv = rng.standard_normal((batch, units, T, rank), dtype=np.float32)
@@ -122,7 +122,7 @@ def hadamard_mixed(h: np.ndarray, B: np.ndarray) -> tuple[np.ndarray, np.ndarray
     H = sylvester(r) / np.sqrt(r)
     hm = (h.astype(np.float64) @ H).astype(np.float32)
     Bm = np.einsum("ij,ujw->uiw", H, B.astype(np.float64)).astype(np.float16)
-    return hm, Bm
+    return hm, np.ascontiguousarray(Bm)
 
 
 def queries(seed: int, batch: int, heads: int, dim: int, scale: float = 1.0) -> np.ndarray:
