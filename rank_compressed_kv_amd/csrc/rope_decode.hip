@@ -18,6 +18,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace lrkv {
 
 struct RopeArgs {
@@ -283,11 +285,12 @@ __global__ __launch_bounds__(256, 2) void rope_decode(const RopeArgs p) {
 // = 256 registers per lane, resident in the accumulation registers and read
 // there by the MFMAs. A lane's eight cos/sin pairs (its token, its
 // frequencies) serve all four heads, so the per-tile angle rotation is shared.
-// Iteration i of the tile loop is one instruction stream:
-//   * RoPE combine of tile i-1's accumulators into per-wave partial scores,
-//     which go to LDS;
-//   * tile i's 64 score MFMAs (4 heads x 16 K steps) in 16 slices, each slice
-//     carrying a share of the vector work: the softmax of tile i-2 for head w
+// Iteration i of the tile loop is one instruction stream: tile i's 64 score
+// MFMAs (4 heads x 16 K steps) in 16 slices, into the accumulators of tile
+// parity i & 1, each slice carrying a share of the vector work:
+//   * the RoPE combine of tile i-1 (the other parity's accumulators), one head
+//     per slice, into per-wave partial scores, which go to LDS;
+//   * the softmax of tile i-2 for head w
 //     (sum of the four waves' partials; p and the rescale factor to LDS), the
 //     angle rotation, and the value product of tile i-3 for all four heads on
 //     16x16x32 MFMAs (wave w owns latent dims [64 w, 64 w + 64));
@@ -298,7 +301,9 @@ __global__ __launch_bounds__(256, 2) void rope_decode(const RopeArgs p) {
 // orders every exchange. Loads go buffer->LDS, keys three tiles ahead (four
 // buffers) and values one tile ahead of tile i (five buffers: the value product
 // lags three tiles); every wave issues exactly 8 loads per tile, so the waits
-// count loads:
+// count loads (the wait at the top of iteration i completes every wave's keys of
+// tiles i and i+1, so the first fragments of tile i+1 are read at the end of
+// iteration i):
 //   keys   rows of 512 B with the 16-byte chunks of row t stored at
 //          chunk ^ (t & 15), so that B-fragment reads (16 lanes = 16 rows, one
 //          chunk) hit distinct banks; one 1 KB load writes two rows; the key
@@ -429,17 +434,22 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
     floatx4 o[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) o[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    floatx16 acc[NH];
+    // score accumulators by tile parity: tile i's MFMAs write acc[i & 1] while the
+    // combine of tile i-1 reads acc[(i - 1) & 1]
+    floatx16 acc[2][NH];
+    half8 bq[AH];                              // the next tile's first key fragments
 
-    // RoPE combine of head h: the lane's 16 features x cos/sin.
-    auto combine = [&](int h) -> float {
+    // RoPE combine of head h of the tile with parity PAR (a compile-time constant,
+    // so that the accumulators stay in registers): the lane's 16 features x cos/sin.
+    auto combine = [&](auto PAR, int h) __attribute__((always_inline)) -> float {
+        constexpr int par = decltype(PAR)::value;
         float x = 0.0f, y = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
-            x = fmaf(cs[k], acc[h][2 * k], x);
-            x = fmaf(sn[k], acc[h][2 * k + 1], x);
-            y = fmaf(cs[k + 1], acc[h][2 * k + 2], y);
-            y = fmaf(sn[k + 1], acc[h][2 * k + 3], y);
+            x = fmaf(cs[k], acc[par][h][2 * k], x);
+            x = fmaf(sn[k], acc[par][h][2 * k + 1], x);
+            y = fmaf(cs[k + 1], acc[par][h][2 * k + 2], y);
+            y = fmaf(sn[k + 1], acc[par][h][2 * k + 3], y);
         }
         return x + y;
     };
@@ -487,7 +497,6 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
     };
     auto score_mfma = [&](int tile) {
         const half_t* kt = ktile[tile % NBK];
-        half8 bq[AH];
 #pragma unroll
         for (int a = 0; a < AH; ++a) bq[a] = kfrag(kt, a);
 #pragma unroll
@@ -495,7 +504,7 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
             const half8 cur = bq[ks % AH];
             if (ks + AH < KS) bq[ks % AH] = kfrag(kt, ks + AH);
 #pragma unroll
-            for (int h = 0; h < NH; ++h) acc[h] = mfma32(qf[h][ks], cur, ks == 0 ? floatx16{} : acc[h]);
+            for (int h = 0; h < NH; ++h) acc[0][h] = mfma32(qf[h][ks], cur, ks == 0 ? floatx16{} : acc[0][h]);
         }
     };
 
@@ -512,21 +521,20 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
     issue_keys(3);
     issue_values(1);
     score_mfma(0);
-    for (int i = 1; i < n_tiles; ++i) {
-        asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    // tile 1's keys came with the prologue (complete and visible since its barrier)
+    if (n_tiles > 1) {
+#pragma unroll
+        for (int a = 0; a < AH; ++a) bq[a] = kfrag(ktile[1 % NBK], a);
+    }
+    // iteration i (parity PAR = i & 1 as a compile-time constant)
+    auto iteration = [&](int i, auto PAR) __attribute__((always_inline)) {
+        constexpr int cur_p = decltype(PAR)::value, prv_p = cur_p ^ 1;
+        // every wave's keys of tiles i and i+1 are complete: the loads after the
+        // keys of tile i+1 (issued two iterations ago) are at most 12
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
         __syncthreads();
         float ps[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            ps[h] = combine(h);
-            // the first MFMA of head h (it overwrites acc[h]) now depends on the
-            // combine, so the accumulator registers are reused in place
-            asm("" : "+a"(qf[h][0]) : "v"(ps[h]));
-        }
         const half_t* kt = ktile[i % NBK];
-        half8 bq[AH];
-#pragma unroll
-        for (int a = 0; a < AH; ++a) bq[a] = kfrag(kt, a);
         float s = 0.0f, tmax = 0.0f;
         half8 pf = {}, va[2] = {};
         float al = 1.0f;
@@ -537,30 +545,34 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
             const half8 cur = bq[ks % AH];
             if (ks + AH < KS) bq[ks % AH] = kfrag(kt, ks + AH);
 #pragma unroll
-            for (int h = 0; h < NH; ++h) acc[h] = mfma32(qf[h][ks], cur, ks == 0 ? floatx16{} : acc[h]);
-            if (ks == 0) {
+            for (int h = 0; h < NH; ++h)
+                acc[cur_p][h] = mfma32(qf[h][ks], cur, ks == 0 ? floatx16{} : acc[cur_p][h]);
+            // combine of tile i-1, one head per slice, beside this tile's MFMAs
+            if (ks < NH) {
+                ps[ks] = combine(std::integral_constant<int, prv_p>{}, ks);
+            } else if (ks == 4) {
                 write_partials(i - 1, ps, false);
                 s = read_scores(st);
-            } else if (ks == 1) {
+            } else if (ks == 5) {
                 tmax = fmaxf(s, dppf<0xB1>(s));
                 tmax = fmaxf(tmax, dppf<0x4E>(tmax));
-            } else if (ks == 2) {
+            } else if (ks == 6) {
                 tmax = fmaxf(tmax, dppf<0x141>(tmax));
                 tmax = fmaxf(tmax, dppf<0x140>(tmax));
                 tmax = rowpair(tmax, true);
-            } else if (ks == 3) {
+            } else if (ks == 7) {
                 softmax_update(st, s, tmax);
-            } else if (ks == 4 || ks == 5) {
-                rotate4(cs + 4 * (ks - 4), sn + 4 * (ks - 4), stp + 4 * (ks - 4));
+            } else if (ks == 8 || ks == 9) {
+                rotate4(cs + 4 * (ks - 8), sn + 4 * (ks - 8), stp + 4 * (ks - 8));
             }
             // value product of tile i-3
-            if (ks == 6) {
+            if (ks == 10) {
                 pf = *reinterpret_cast<const half8*>(&pbuf[vt_tile & 1][l & 15][8 * (l >> 4)]);
                 al = abuf[vt_tile & 1][l & 15];
             }
-            if (ks >= 6 && ks < 10) va[ks & 1] = *reinterpret_cast<const half8*>(vt + 512 * (ks - 6));
-            if (ks >= 7 && ks < 11) {
-                const int m = ks - 7;
+            if (ks >= 10 && ks < 14) va[ks & 1] = *reinterpret_cast<const half8*>(vt + 512 * (ks - 10));
+            if (ks >= 11 && ks < 15) {
+                const int m = ks - 11;
                 o[m] = mfma16(va[m & 1], pf, o[m] * al);
             }
             // keys of tile i+3 (their buffer was last read by tile i-1's MFMAs) and
@@ -572,14 +584,28 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
             if (ks >= 8 && (ks & 1)) value_load(i + 1, (ks - 8) >> 1);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the next tile's first fragments (its keys are complete since this
+        // iteration's barrier; their buffer is rewritten two iterations later)
+        if (i + 1 < n_tiles) {
+#pragma unroll
+            for (int a = 0; a < AH; ++a) bq[a] = kfrag(ktile[(i + 1) % NBK], a);
+        }
+    };
+    int it = 1;
+    for (; it + 1 < n_tiles; it += 2) {
+        iteration(it, std::integral_constant<int, 1>{});
+        iteration(it + 1, std::integral_constant<int, 0>{});
     }
+    if (it < n_tiles) iteration(it, std::integral_constant<int, 1>{});
     wait_vmem();                               // the loads past the last tile (empty)
     // drain: partials of the last tile; softmax of the last two tiles; value
     // products of the last three, each exchange separated by a barrier
     {
         float ps[NH];
 #pragma unroll
-        for (int h = 0; h < NH; ++h) ps[h] = combine(h);
+        for (int h = 0; h < NH; ++h)
+            ps[h] = ((n_tiles - 1) & 1) ? combine(std::integral_constant<int, 1>{}, h)
+                                        : combine(std::integral_constant<int, 0>{}, h);
         write_partials(n_tiles - 1, ps, true);
     }
     __syncthreads();
