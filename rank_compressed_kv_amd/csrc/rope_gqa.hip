@@ -33,6 +33,11 @@
 //                   the M-tile's 32-dim group), transposed through LDS.
 // int4 codes (two's complement nibbles) become fp16 with the offset-1024
 // exponent trick: exact integers, then x scale (keys) rounded once to fp16.
+// int4 super-tiles: with 4 query heads and 16 score columns, four consecutive
+// tiles share one score accumulator, tile j in columns 4j..4j+3 (its queries are
+// zero elsewhere); softmax and value scaling then run once per four tiles, and a
+// tile's value product follows four tiles after its scores, with p passed by its
+// own column group only. Each head's output is the sum of its four columns.
 #include "tiles.h"
 
 #include <math.h>
@@ -137,36 +142,40 @@ template <int R, bool INT4>
 struct GqaTile;
 
 // int4 tiles stream into LDS with direct buffer loads (no registers), several
-// tiles ahead. Slot layout (bytes): key codes [32 tok][R/2] | value codes
-// [R dims][16] | key scales [32 tok][R/32] | value scales [R/32][32 tok].
+// tiles ahead, into two rings: a key slot holds key codes [32 tok][R/2] | key
+// scales [32 tok][R/32]; a value slot value codes [R dims][16] | value scales
+// [R/32][32 tok]. Key slots are free once the tile is scored, value slots only
+// after its value product, which runs a few tiles later.
 template <int R>
 struct GqaTile<R, true> {
     static constexpr int KS = R / 32, VM = R / 16, NG = R / 32;
     static constexpr int KB = 32 * R / 2, VB = R * 16, SB = 32 * NG * 2;
-    static constexpr int SLOT = KB + VB + 2 * SB;
+    static constexpr int KSLOT = KB + SB, VSLOT = VB + SB;
     uint32_t kc[2][KS];      // key codes of token 16 nb + c, ranks [R/4 g, R/4 (g+1))
     uint32_t ks0, ks1;       // key scale of those ranks (fp16 bits), N-blocks 0 and 1
-    uint32_t vc[VM];         // value codes of dim 16 mv + c, tokens 8g..8g+7
-    uint2 vs[NG][2];         // value scales of tokens 16 nb + 4g + (0..3), per 32-dim group
 
-    // Issue the loads of cache block `blk` of the unit into `slot` (4 loads; a
-    // negative blk reads past every buffer's end, i.e. zeros, so that every tile
-    // issues the same number of loads).
-    __device__ __forceinline__ static void issue(const int32x4* rs, int blk, const uint8_t* slot, int l) {
+    // Issue the loads of cache block `blk` of the unit (4 loads; a negative blk
+    // reads past every buffer's end, i.e. zeros, so that every tile issues the
+    // same number of loads).
+    __device__ __forceinline__ static void issue(const int32x4* rs, int blk, const uint8_t* kslot,
+                                                 const uint8_t* vslot, int l) {
         const uint32_t bad = 0x80000000u;
         const bool ok = blk >= 0;
         constexpr uint64_t all = ~0ull, ks_lanes = (1ull << (SB / 16)) - 1;
-        buf_dma16_lanes(rs[0], ok ? (uint32_t)blk * KB + 16 * l : bad, slot,
+        buf_dma16_lanes(rs[0], ok ? (uint32_t)blk * KB + 16 * l : bad, kslot,
                         KB / 16 >= 64 ? all : (1ull << (KB / 16)) - 1);
-        buf_dma16_lanes(rs[1], ok ? (uint32_t)blk * VB + 16 * l : bad, slot + KB,
+        buf_dma16_lanes(rs[1], ok ? (uint32_t)blk * VB + 16 * l : bad, vslot,
                         VB / 16 >= 64 ? all : (1ull << (VB / 16)) - 1);
-        buf_dma16_lanes(rs[2], ok ? (uint32_t)blk * SB + 16 * l : bad, slot + KB + VB, ks_lanes);
-        buf_dma16_lanes(rs[3], ok ? (uint32_t)blk * SB + 16 * l : bad, slot + KB + VB + SB, ks_lanes);
+        buf_dma16_lanes(rs[2], ok ? (uint32_t)blk * SB + 16 * l : bad, kslot + KB, ks_lanes);
+        buf_dma16_lanes(rs[3], ok ? (uint32_t)blk * SB + 16 * l : bad, vslot + VB, ks_lanes);
     }
-    __device__ __forceinline__ void read_keys(const uint8_t* slot, int c, int g) {
+    // `valid`: tokens of the tile before the chunk's end. The key scales of the
+    // others are zeroed (an unwritten scale may hold anything, and these keys
+    // meet zero queries in other tiles' score columns, where inf x 0 would spread).
+    __device__ __forceinline__ void read_keys(const uint8_t* kslot, int c, int g, int valid) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            const uint8_t* src = slot + (16 * nb + c) * (R / 2) + (R / 8) * g;
+            const uint8_t* src = kslot + (16 * nb + c) * (R / 2) + (R / 8) * g;
             if constexpr (KS == 2) {
                 const uint2 v = *reinterpret_cast<const uint2*>(src);
                 kc[nb][0] = v.x;
@@ -175,30 +184,20 @@ struct GqaTile<R, true> {
                 kc[nb][0] = *reinterpret_cast<const uint32_t*>(src);
             }
         }
-        const uint16_t* ksp = reinterpret_cast<const uint16_t*>(slot + KB + VB) + c * NG + (R / 4) * g / 32;
-        ks0 = ksp[0];
-        ks1 = ksp[16 * NG];
-    }
-    __device__ __forceinline__ void read_values(const uint8_t* slot, int c, int g) {
-#pragma unroll
-        for (int mv = 0; mv < VM; ++mv)
-            vc[mv] = *reinterpret_cast<const uint32_t*>(slot + KB + (16 * mv + c) * 16 + 4 * g);
-#pragma unroll
-        for (int gr = 0; gr < NG; ++gr)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                vs[gr][nb] = *reinterpret_cast<const uint2*>(slot + KB + VB + SB + (gr * 32 + 16 * nb + 4 * g) * 2);
+        const uint16_t* ksp = reinterpret_cast<const uint16_t*>(kslot + KB) + c * NG + (R / 4) * g / 32;
+        ks0 = c < valid ? ksp[0] : 0u;
+        ks1 = 16 + c < valid ? ksp[16 * NG] : 0u;
     }
     __device__ __forceinline__ half8 key_operand(int nb, int k, uint32_t magic) const {
         return dequant_keys(kc[nb][k], nb ? ks1 : ks0, magic);
     }
-    // codes in the unpack order: element p is token 8g + (0, 4, 1, 5, 2, 6, 3, 7)[p]
-    __device__ __forceinline__ half8 value_operand(int mv, uint32_t magic) const {
-        return value_codes(vc[mv], magic);
+    // value codes of dim 16 mv + c, tokens 8g..8g+7
+    __device__ __forceinline__ static uint32_t value_word(const uint8_t* vslot, int mv, int c, int g) {
+        return *reinterpret_cast<const uint32_t*>(vslot + (16 * mv + c) * 16 + 4 * g);
     }
-    // (p_i, p_i+1) x value scales of tokens 16 nb + 4g + i, i + 1 (i = 2 j)
-    __device__ __forceinline__ half2_t scale_pair(int gr, int nb, int j, half2_t pp) const {
-        return pp * __builtin_bit_cast(half2_t, j ? vs[gr][nb].y : vs[gr][nb].x);
+    // value scales (fp16) of tokens 16 nb + 4g + (0..3), 32-dim group gr
+    __device__ __forceinline__ static uint2 value_scales(const uint8_t* vslot, int gr, int nb, int g) {
+        return *reinterpret_cast<const uint2*>(vslot + VB + (gr * 32 + 16 * nb + 4 * g) * 2);
     }
 };
 
@@ -240,14 +239,22 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     static_assert(R == 32 || R == 64, "rank 32 or 64");
     static_assert(NH >= 1 && NH <= 16, "1..16 query heads per KV head");
     using Tile = GqaTile<R, INT4>;
-    // per wave, two buffers: rotated queries, one u32 fp16 pair per (head,
-    // frequency), plus a zero row for the padding heads
-    __shared__ __attribute__((aligned(16))) uint32_t qt_s[4][2][(NH + 1) * 64];
-    // int4: per-wave ring of tile slots filled by direct loads kDepth tiles
-    // ahead; a tile's slot is read twice (keys, then values one tile later)
-    constexpr int kDepth = 4, kSlots = kDepth + 2;
-    constexpr int kSlotBytes = INT4 ? GqaTile<R, true>::SLOT : 16;
-    __shared__ __attribute__((aligned(16))) uint8_t ring_s[4][INT4 ? kSlots : 1][kSlotBytes];
+    // int4 works in super-tiles of S = 16 / NH tiles whose NH heads fill the 16
+    // score columns: column c = NH j + h is head h of the super-tile's tile j.
+    constexpr int S = INT4 ? 16 / NH : 1;
+    static_assert(!INT4 || NH == 4, "int4 super-tiles are laid out for 4 heads per KV head");
+    // per wave, rotated queries, one u32 fp16 pair per (row, frequency): int4 one
+    // buffer with row NH j + h for tile j of the super-tile, fp16 two buffers of
+    // NH rows; then a zero row for the padding columns
+    constexpr int kQRows = NH * S + 1, kQBufs = INT4 ? 1 : 2, kZeroRow = NH * S;
+    __shared__ __attribute__((aligned(16))) uint32_t qt_s[4][kQBufs][kQRows * 64];
+    // int4: per-wave rings filled by direct loads kDepth tiles ahead; a tile's key
+    // slot is free once it is scored, its value slot after its value product, S
+    // tiles later (its value scales are read by the super-tile's softmax)
+    constexpr int kDepth = 3, kKeySlots = kDepth + 1, kValSlots = kDepth + S + 1;
+    constexpr int kKSlot = INT4 ? GqaTile<R, true>::KSLOT : 16, kVSlot = INT4 ? GqaTile<R, true>::VSLOT : 16;
+    __shared__ __attribute__((aligned(16))) uint8_t kring_s[4][INT4 ? kKeySlots : 1][kKSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t vring_s[4][INT4 ? kValSlots : 1][kVSlot];
 
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), l = threadIdx.x & 63;
     const int gw = blockIdx.x * 4 + w;
@@ -267,8 +274,8 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     }
     const int c = l & 15, g = l >> 4;
     const int hrow = c < NH ? c : NH;
-    qt_s[w][0][NH * 64 + l] = 0u;
-    qt_s[w][1][NH * 64 + l] = 0u;
+#pragma unroll
+    for (int qb = 0; qb < kQBufs; ++qb) qt_s[w][qb][kZeroRow * 64 + l] = 0u;
     const uint32_t magic = 0x64006400u;
     const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
     const int t_last = t_begin + kTile * (n_tiles - 1);
@@ -279,7 +286,8 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     // tiles i+1..i+kDepth-1 in flight; the set-up loads are all waited for
     // before the loop, and no other vector-memory operation is issued in it.
     int32x4 rs[4];
-    uint8_t* ring = &ring_s[w][0][0];
+    uint8_t* kring = &kring_s[w][0][0];
+    uint8_t* vring = &vring_s[w][0][0];
     const int blk0 = t_begin / kTile;
     if constexpr (INT4) {
         const long nblk = p.cap / kTile;
@@ -288,7 +296,8 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
         rs[2] = make_rsrc((const uint8_t*)p.sk + bu * nblk * Tile::SB, (uint32_t)(nblk * Tile::SB));
         rs[3] = make_rsrc((const uint8_t*)p.sv + bu * nblk * Tile::SB, (uint32_t)(nblk * Tile::SB));
 #pragma unroll
-        for (int i = 0; i < kDepth; ++i) Tile::issue(rs, i < n_tiles ? blk0 + i : -1, ring + i * kSlotBytes, l);
+        for (int i = 0; i < kDepth; ++i)
+            Tile::issue(rs, i < n_tiles ? blk0 + i : -1, kring + i * kKSlot, vring + i * kVSlot, l);
     }
 
     // B^k fragments: A[dim 16 mt + c][ranks R/4 g + 8 ks + perm(0..7)]
@@ -334,24 +343,24 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     for (int mv = 0; mv < VM; ++mv) accv[mv] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // Q~ = R(t0 - q_pos)^T q of the next tile for every head, (c qa + s qb,
-    // c qb - s qa), into query buffer `qb_i`; the rotation then advances a tile.
-    auto rotate_queries = [&](int qb_i) __attribute__((always_inline)) {
-        uint32_t* qt = qt_s[w][qb_i];
+    // c qb - s qa), into rows row0 .. row0 + NH - 1 of `qt`; the rotation then
+    // advances a tile.
+    auto rotate_queries = [&](uint32_t* qt, int row0) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             const float ta = fmaf(ang.x, qa[h], ang.y * qb[h]);
             const float tb = fmaf(ang.x, qb[h], -ang.y * qa[h]);
-            qt[h * 64 + l] = __builtin_bit_cast(uint32_t, pack2(ta, tb));
+            qt[(row0 + h) * 64 + l] = __builtin_bit_cast(uint32_t, pack2(ta, tb));
         }
         ang = cmul(ang, stp);
     };
-    // Reconstruction, rotation by R(tau) and scores of one tile, with the
-    // queries of buffer qb_i: sacc[nb][i] = score of head c, token 16 nb + 4 g + i.
-    auto scores = [&](const Tile& T, int qb_i, floatx4* sacc) __attribute__((always_inline)) {
-        const uint32_t* qt = qt_s[w][qb_i];
+    // Reconstruction, rotation by R(tau) and scores of one tile against query row
+    // `row` of `qt` (the lane's column): sacc[nb][i] (+)= score of that row at token
+    // 16 nb + 4 g + i. With `zero` the accumulators start from zero.
+    auto scores = [&](const Tile& T, const uint32_t* qt, int row, floatx4* sacc, bool zero) __attribute__((always_inline)) {
         half8 bq[4];
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) bq[k2] = *reinterpret_cast<const half8*>(qt + hrow * 64 + 16 * k2 + 4 * g);
+        for (int k2 = 0; k2 < 4; ++k2) bq[k2] = *reinterpret_cast<const half8*>(qt + row * 64 + 16 * k2 + 4 * g);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             floatx4 acc[8];
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt) acc[mt] = mfma16(af[mt][k], hop, acc[mt]);
             }
-            sacc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (zero) sacc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 half2_t a2[4];
@@ -373,106 +382,178 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
             }
         }
     };
-    // Online softmax of one tile's scores, p' = p x value scale (fp16), and
-    // the value product. TAIL: the tile may end past t_end (masks on).
-    auto softmax_values = [&](const Tile& T, const floatx4* sacc, int t0, auto tail_flag) __attribute__((always_inline)) {
-        constexpr bool TAIL = decltype(tail_flag)::value;
-        float sv[8];
+
+    if constexpr (INT4) {
+        // Sub-step i scores tile i (j = i % S of its super-tile) into the columns
+        // of group j: the other columns read the zero query row, so they add
+        // nothing. The value product of tile i - S runs in the same sub-step with
+        // p' of its super-tile, whose softmax ran at the end of that super-tile.
+        uint32_t* qt = qt_s[w][0];
+        const int col_tile = c / NH;               // the lane's tile within a super-tile
+        const int n_sub = (n_tiles + S - 1) / S * S;
+        floatx4 sacc[2] = {};
+        half8 bp[NG] = {};                         // p' (value B operand) of the lane's column
+        // Online softmax over one super-tile (tiles ts..ts+S-1, starting at token
+        // t0s): lane (c, g) holds head c % NH of tile c / NH at tokens 16 nb + 4 g + i.
+        // p x the token's value scale becomes bp; the output is rescaled.
+        auto softmax_super = [&](int ts) __attribute__((always_inline)) {
+            const int tl = t_begin + kTile * (ts + col_tile);    // the lane's tile start
+            float sv[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sv[k] = sacc[k >> 2][k & 3];
-        if constexpr (TAIL) {
+            for (int k = 0; k < 8; ++k) {
+                sv[k] = sacc[k >> 2][k & 3];
+                if (tl + 16 * (k >> 2) + 4 * g + (k & 3) >= t_end) sv[k] = -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mx = xrow_max(mx);
+            mx = fmaxf(mx, dppf<0x124>(mx));       // row_ror:4 and :8, the head's other tiles
+            mx = fmaxf(mx, dppf<0x128>(mx));
+            const float mn = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+            float pr[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (t0 + 16 * (k >> 2) + 4 * g + (k & 3) >= t_end) sv[k] = -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mx = xrow_max(mx);
-        const float mn = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        float pr[8];
+            for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(sv[k] - mn);
+            float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+            ps = xrow_sum(ps);
+            ps += dppf<0x124>(ps);
+            ps += dppf<0x128>(ps);
+            l_run = fmaf(l_run, alpha, ps);
+            m_run = mn;
+            const uint8_t* vsl = vring + ((ts + col_tile) % kValSlots) * kVSlot;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(sv[k] - mn);
-        const float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-        l_run = fmaf(l_run, alpha, xrow_sum(ps));
-        m_run = mn;
-        half8 bp[NG];
+            for (int gr = 0; gr < NG; ++gr) {
+                uint32_t x[2][2];
 #pragma unroll
-        for (int gr = 0; gr < NG; ++gr) {
-            uint32_t x[2][2];
+                for (int nb = 0; nb < 2; ++nb) {
+                    const uint2 sc = Tile::value_scales(vsl, gr, nb, g);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    half2_t q2 = T.scale_pair(gr, nb, j, pack2(pr[4 * nb + 2 * j], pr[4 * nb + 2 * j + 1]));
-                    if constexpr (TAIL && INT4) {
+                    for (int j = 0; j < 2; ++j) {
+                        half2_t q2 = pack2(pr[4 * nb + 2 * j], pr[4 * nb + 2 * j + 1]) *
+                                     __builtin_bit_cast(half2_t, j ? sc.y : sc.x);
                         // an unwritten scale past t_end may hold anything; p there is 0
-                        const int tk = t0 + 16 * nb + 4 * g + 2 * j;
+                        const int tk = tl + 16 * nb + 4 * g + 2 * j;
                         if (tk >= t_end) q2.x = (half_t)0.0f;
                         if (tk + 1 >= t_end) q2.y = (half_t)0.0f;
+                        x[nb][j] = __builtin_bit_cast(uint32_t, q2);
                     }
-                    x[nb][j] = __builtin_bit_cast(uint32_t, q2);
                 }
-            bp[gr] = p_operand<INT4>(x[0][0], x[0][1], x[1][0], x[1][1]);
-        }
-#pragma unroll
-        for (int mv = 0; mv < VM; ++mv) {
-            half8 va = T.value_operand(mv, magic);
-            if constexpr (TAIL && !INT4) {
-                // fp16 values past t_end may hold anything (their p is zero)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (t0 + 8 * g + e >= t_end) va[e] = (half_t)0.0f;
+                bp[gr] = p_operand<true>(x[0][0], x[0][1], x[1][0], x[1][1]);
             }
-            accv[mv] *= alpha;
-            accv[mv] = mfma16(va, bp[INT4 ? mv / 2 : 0], accv[mv]);
-        }
-    };
+#pragma unroll
+            for (int mv = 0; mv < VM; ++mv) accv[mv] *= alpha;
+        };
+        // value product of tile t (position j in its super-tile): only the lanes of
+        // column group j pass their p', the others zero
+        auto values_sub = [&](int t, int j) __attribute__((always_inline)) {
+            const uint8_t* vsl = vring + (t % kValSlots) * kVSlot;
+            const bool mine = col_tile == j;
+#pragma unroll
+            for (int mv = 0; mv < VM; ++mv) {
+                const half8 va = value_codes(Tile::value_word(vsl, mv, c, g), magic);
+                const half8 pb = mine ? bp[mv / 2] : half8{};
+                accv[mv] = mfma16(va, pb, accv[mv]);
+            }
+        };
 
-    rotate_queries(0);
-    wave_lds_sync();
-    if constexpr (INT4) {
-        // Two-stage pipeline: iteration i scores tile i while it runs the
-        // softmax and value product of tile i - 1 (independent instruction
-        // streams for the scheduler). Tile i sits in slot i % kSlots.
-        Tile tk, tv;
-        floatx4 sp[2], sc[2];
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(4 * (kDepth - 1)) : "memory");
-        tk.read_keys(ring, c, g);
-        Tile::issue(rs, kDepth < n_tiles ? blk0 + kDepth : -1, ring + kDepth * kSlotBytes, l);
-        scores(tk, 0, sp);
-        rotate_queries(1);
+        rotate_queries(qt, 0);
         wave_lds_sync();
-        int rd = 1, wr = kDepth + 1, pv = 0;      // slots of tile i, tile i + kDepth, tile i - 1
-        for (int i = 1; i < n_tiles; ++i) {
+        for (int i = 0; i < n_sub; ++i) {
+            const int j = i % S;
+            // tile i's loads are complete when at most the kDepth - 1 tiles after it
+            // are in flight
             asm volatile("s_waitcnt vmcnt(%0)" :: "n"(4 * (kDepth - 1)) : "memory");
-            tk.read_keys(ring + rd * kSlotBytes, c, g);
-            tv.read_values(ring + pv * kSlotBytes, c, g);
-            Tile::issue(rs, i + kDepth < n_tiles ? blk0 + i + kDepth : -1, ring + wr * kSlotBytes, l);
+            Tile tk;
+            tk.read_keys(kring + (i % kKeySlots) * kKSlot, c, g, t_end - (t_begin + kTile * i));
+            Tile::issue(rs, i + kDepth < n_tiles ? blk0 + i + kDepth : -1, kring + ((i + kDepth) % kKeySlots) * kKSlot,
+                        vring + ((i + kDepth) % kValSlots) * kVSlot, l);
             // the MFMA-heavy phase issues at raised priority, so that the other
             // wave on this SIMD fills its gaps with vector work
             __builtin_amdgcn_s_setprio(2);
-            scores(tk, i & 1, sc);
+            scores(tk, qt, col_tile == j ? c : kZeroRow, sacc, j == 0);
             __builtin_amdgcn_s_setprio(0);
-            rotate_queries((i + 1) & 1);
-            softmax_values(tv, sp, t_begin + kTile * (i - 1), Flag<false>{});
-            sp[0] = sc[0];
-            sp[1] = sc[1];
-            pv = rd;
-            rd = rd == kSlots - 1 ? 0 : rd + 1;
-            wr = wr == kSlots - 1 ? 0 : wr + 1;
+            rotate_queries(qt, NH * ((i + 1) % S));
+            if (i >= S) values_sub(i - S, j);
+            if (j == S - 1) softmax_super(i - (S - 1));
             wave_lds_sync();
         }
-        tv.read_values(ring + pv * kSlotBytes, c, g);
-        softmax_values(tv, sp, t_last, Flag<true>{});
+#pragma unroll
+        for (int j = 0; j < S; ++j) values_sub(n_sub - S + j, j);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // each head's output is spread over its S columns: sum them
+#pragma unroll
+        for (int mv = 0; mv < VM; ++mv)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = accv[mv][i];
+                v += dppf<0x124>(v);
+                v += dppf<0x128>(v);
+                accv[mv][i] = v;
+            }
     } else {
+        rotate_queries(qt_s[w][0], 0);
+        wave_lds_sync();
+        // Online softmax of one tile's scores, p' = p x value scale (fp16), and
+        // the value product. TAIL: the tile may end past t_end (masks on).
+        auto softmax_values = [&](const Tile& T, const floatx4* sacc, int t0, auto tail_flag) __attribute__((always_inline)) {
+            constexpr bool TAIL = decltype(tail_flag)::value;
+            float sv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sv[k] = sacc[k >> 2][k & 3];
+            if constexpr (TAIL) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (t0 + 16 * (k >> 2) + 4 * g + (k & 3) >= t_end) sv[k] = -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mx = xrow_max(mx);
+            const float mn = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+            float pr[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(sv[k] - mn);
+            const float ps = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+            l_run = fmaf(l_run, alpha, xrow_sum(ps));
+            m_run = mn;
+            half8 bp[NG];
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr) {
+                uint32_t x[2][2];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        half2_t q2 = T.scale_pair(gr, nb, j, pack2(pr[4 * nb + 2 * j], pr[4 * nb + 2 * j + 1]));
+                        if constexpr (TAIL && INT4) {
+                            // an unwritten scale past t_end may hold anything; p there is 0
+                            const int tk = t0 + 16 * nb + 4 * g + 2 * j;
+                            if (tk >= t_end) q2.x = (half_t)0.0f;
+                            if (tk + 1 >= t_end) q2.y = (half_t)0.0f;
+                        }
+                        x[nb][j] = __builtin_bit_cast(uint32_t, q2);
+                    }
+                bp[gr] = p_operand<INT4>(x[0][0], x[0][1], x[1][0], x[1][1]);
+            }
+#pragma unroll
+            for (int mv = 0; mv < VM; ++mv) {
+                half8 va = T.value_operand(mv, magic);
+                if constexpr (TAIL && !INT4) {
+                    // fp16 values past t_end may hold anything (their p is zero)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (t0 + 8 * g + e >= t_end) va[e] = (half_t)0.0f;
+                }
+                accv[mv] *= alpha;
+                accv[mv] = mfma16(va, bp[INT4 ? mv / 2 : 0], accv[mv]);
+            }
+        };
+
         // tiles in pairs through two register buffers (the next tile loads while
         // the current one is processed); the last tile runs with the masks on
         auto step = [&](const Tile& T, int t0, auto tail_flag) __attribute__((always_inline)) {
             floatx4 sacc[2];
-            scores(T, 0, sacc);
+            scores(T, qt_s[w][0], hrow, sacc, true);
             softmax_values(T, sacc, t0, tail_flag);
-            rotate_queries(0);
+            rotate_queries(qt_s[w][0], 0);
             wave_lds_sync();
         };
         Tile ta, tb;

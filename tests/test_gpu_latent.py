@@ -33,6 +33,7 @@ SHAPES = {
     "tiny_glrd": (1, 2, 2, 1, 64, 32, 1e4, 24.0),
     "llama2_glrd": (1, 8, 4, 1, 128, 256, 1e4, 96.0),
     "llama3_gqa": (2, 8, 1, 4, 128, 64, 5e5, 32.0),
+    "llama3_gqa_r32": (2, 8, 1, 4, 128, 32, 5e5, 32.0),
 }
 
 
@@ -188,6 +189,63 @@ def test_rope_gqa_split_independence():
     for o in outs:
         assert rel_l2(o, ref).max() <= TOL
         assert rel_l2(o, outs[0]).max() <= 2 * 2.0 ** -11
+
+
+@pytest.mark.parametrize("fmt_name,n_split", [("int4", 0), ("int4", 3), ("fp16", 0)])
+def test_rope_gqa_rank32(fmt_name, n_split):
+    """Grouped-query units at rank 32 (one 32-element scale group per token)."""
+    R = _R()
+    fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
+    say(f"rope gqa rank 32: {fmt_name} T=900 ragged=(0, 45) n_split={n_split}")
+    c = _make("llama3_gqa_r32", 900, 928, fmt, seed=28, ragged=(0, 45), mixed=fmt_name == "int4")
+    err = rel_l2(_gpu_rope(c, n_split=n_split), _oracle_rope(c))
+    say(f"  max rel-L2 {err.max():.3g}")
+    assert err.max() <= TOL, err.max()
+
+
+def _poison_tail(cache, lens, int4):
+    """Every cache entry at or past its sequence's length becomes NaN (fp16
+    latents and scales) or 0xFF code bytes: memory the caller never wrote."""
+    nan = float("nan")
+    blk = 32
+    for b, n in enumerate(int(x) for x in lens):
+        nb, pos = n // blk, n % blk
+        cache.hk[b, :, n:] = 255 if int4 else nan
+        if int4:
+            cache.sk[b, :, n:] = nan
+            cache.hv[b, :, nb + 1:] = 255
+            cache.sv[b, :, nb + 1:] = nan
+            if nb < cache.sv.shape[2]:
+                cache.hv[b, :, nb, :, (pos + 1) // 2:] = 255
+                cache.sv[b, :, nb, :, pos:] = nan
+        else:
+            cache.hv[b, :, nb + 1:] = nan
+            if nb < cache.hv.shape[2]:
+                cache.hv[b, :, nb, :, pos:] = nan
+
+
+@pytest.mark.parametrize("name,fmt_name,T,cap,ragged,n_split", [
+    ("llama3_gqa", "int4", 1000, 1056, (0, 333), 0),
+    ("llama3_gqa", "int4", 1000, 1056, (17, 333), 3),
+    ("llama3_gqa", "int4", 31, 64, (), 0),
+    ("llama3_gqa_r32", "int4", 700, 736, (0, 5), 0),
+    ("llama3_gqa", "fp16", 1000, 1056, (0, 333), 0),
+])
+def test_rope_gqa_poisoned_tail(name, fmt_name, T, cap, ragged, n_split):
+    """Cache entries past each sequence's end hold NaN: nothing of them may reach
+    the result (several tiles can share one score accumulator, where a NaN key
+    would spread to the other tiles' columns)."""
+    R = _R()
+    fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
+    say(f"rope gqa poisoned tail: {name} {fmt_name} T={T} ragged={ragged} n_split={n_split}")
+    c = _make(name, T, cap, fmt, seed=29, ragged=ragged, mixed=fmt_name == "int4")
+    _poison_tail(c["cache"], c["lens"], fmt_name == "int4")
+    torch.cuda.synchronize()
+    got = _gpu_rope(c, n_split=n_split)
+    assert np.isfinite(got).all()
+    err = rel_l2(got, _oracle_rope(c))
+    say(f"  max rel-L2 {err.max():.3g}")
+    assert err.max() <= TOL, err.max()
 
 
 def test_rope_split_independence():
