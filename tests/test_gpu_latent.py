@@ -230,14 +230,19 @@ def _poison_tail(cache, lens, int4):
     ("llama3_gqa", "int4", 31, 64, (), 0),
     ("llama3_gqa_r32", "int4", 700, 736, (0, 5), 0),
     ("llama3_gqa", "fp16", 1000, 1056, (0, 333), 0),
+    ("llama2_glrd", "fp16", 1500, 1536, (), 0),
+    ("llama2_glrd", "fp16", 1500, 1536, (), 5),
+    ("llama2_glrd", "int4", 700, 736, (), 0),
+    ("tiny_glrd", "fp16", 200, 256, (), 0),
+    ("tiny_glrd", "int4", 201, 256, (), 0),
 ])
-def test_rope_gqa_poisoned_tail(name, fmt_name, T, cap, ragged, n_split):
+def test_rope_poisoned_tail(name, fmt_name, T, cap, ragged, n_split):
     """Cache entries past each sequence's end hold NaN: nothing of them may reach
     the result (several tiles can share one score accumulator, where a NaN key
     would spread to the other tiles' columns)."""
     R = _R()
     fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
-    say(f"rope gqa poisoned tail: {name} {fmt_name} T={T} ragged={ragged} n_split={n_split}")
+    say(f"rope poisoned tail: {name} {fmt_name} T={T} ragged={ragged} n_split={n_split}")
     c = _make(name, T, cap, fmt, seed=29, ragged=ragged, mixed=fmt_name == "int4")
     _poison_tail(c["cache"], c["lens"], fmt_name == "int4")
     torch.cuda.synchronize()
@@ -312,6 +317,31 @@ def test_absorbed_parity(fmt_name, B, T, cap, r, s):
     store = oattn.stored_fp16 if fmt == R.FMT_FP16 else oattn.stored_int4
     ref = oattn.palu_decode_absorbed(store(lay["hk"]), store(lay["hv"]), qa, lens, s, 1, dh)
     err = rel_l2(got.cpu().numpy(), ref)
+    assert err.max() <= TOL, err.max()
+
+
+@pytest.mark.parametrize("fmt_name,B,T,cap,r,s", [("fp16", 3, 700, 736, 256, 4), ("int4", 2, 999, 1024, 256, 4),
+                                                  ("int4", 2, 515, 544, 64, 2), ("fp16", 2, 333, 352, 64, 2)])
+def test_absorbed_poisoned_tail(fmt_name, B, T, cap, r, s):
+    """Absorbed path with NaN (fp16) or 0xFF codes and NaN scales (int4) in every
+    cache entry past each sequence's end."""
+    R = _R()
+    fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
+    say(f"absorbed poisoned tail: {fmt_name} B={B} T={T} r={r} heads/unit={s}")
+    U, dh = 8, 128
+    lay = synth.latent_layer(33, B, U, T, r, s * dh, 96.0)
+    qa = synth.queries(34, B, U * s, r, 3.0)
+    cache = R.LatentCache(B, U, s, 1, dh, r, cap, fmt, 0.0)
+    cache.append(to_dev(lay["hk"]), to_dev(lay["hv"]))
+    lens = np.array([T - 53 * b for b in range(B)])
+    cache.lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    cache.host_lens[:] = lens
+    _poison_tail(cache, lens, fmt_name == "int4")
+    got = cache.decode(R.MODE_ABSORBED, to_dev(qa)).cpu().numpy()
+    assert np.isfinite(got).all()
+    store = oattn.stored_fp16 if fmt == R.FMT_FP16 else oattn.stored_int4
+    ref = oattn.palu_decode_absorbed(store(lay["hk"]), store(lay["hv"]), qa, lens, s, 1, dh)
+    err = rel_l2(got, ref)
     assert err.max() <= TOL, err.max()
 
 
