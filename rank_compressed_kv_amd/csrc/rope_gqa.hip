@@ -144,7 +144,9 @@ struct GqaTile;
 // int4 tiles stream into LDS with direct buffer loads (no registers), several
 // tiles ahead, into two rings: a key slot holds key codes [32 tok][R/2] | key
 // scales [32 tok][R/32]; a value slot value codes [R dims][16] | value scales
-// [R/32][32 tok]. Key slots are free once the tile is scored, value slots only
+// [R/32][32 tok]. At rank 64 a token's two 16-byte code chunks swap places in
+// rows t with bit 2 of t set (the load picks its source chunk accordingly), so
+// that the 16 rows one key read touches spread over all banks. Key slots are free once the tile is scored, value slots only
 // after its value product, which runs a few tiles later.
 template <int R>
 struct GqaTile<R, true> {
@@ -162,7 +164,7 @@ struct GqaTile<R, true> {
         const uint32_t bad = 0x80000000u;
         const bool ok = blk >= 0;
         constexpr uint64_t all = ~0ull, ks_lanes = (1ull << (SB / 16)) - 1;
-        buf_dma16_lanes(rs[0], ok ? (uint32_t)blk * KB + 16 * l : bad, kslot,
+        buf_dma16_lanes(rs[0], ok ? (uint32_t)blk * KB + 16 * (KS == 2 ? l ^ ((l >> 3) & 1) : l) : bad, kslot,
                         KB / 16 >= 64 ? all : (1ull << (KB / 16)) - 1);
         buf_dma16_lanes(rs[1], ok ? (uint32_t)blk * VB + 16 * l : bad, vslot,
                         VB / 16 >= 64 ? all : (1ull << (VB / 16)) - 1);
@@ -175,7 +177,9 @@ struct GqaTile<R, true> {
     __device__ __forceinline__ void read_keys(const uint8_t* kslot, int c, int g, int valid) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            const uint8_t* src = kslot + (16 * nb + c) * (R / 2) + (R / 8) * g;
+            const int t = 16 * nb + c;
+            const uint8_t* src = KS == 2 ? kslot + 16 * (2 * t + ((g >> 1) ^ ((t >> 2) & 1))) + 8 * (g & 1)
+                                         : kslot + t * (R / 2) + (R / 8) * g;
             if constexpr (KS == 2) {
                 const uint2 v = *reinterpret_cast<const uint2*>(src);
                 kc[nb][0] = v.x;
@@ -246,8 +250,10 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     // per wave, rotated queries, one u32 fp16 pair per (row, frequency): int4 one
     // buffer with row NH j + h for tile j of the super-tile, fp16 two buffers of
     // NH rows; then a zero row for the padding columns
-    constexpr int kQRows = NH * S + 1, kQBufs = INT4 ? 1 : 2, kZeroRow = NH * S;
-    __shared__ __attribute__((aligned(16))) uint32_t qt_s[4][kQBufs][kQRows * 64];
+    // rows 80 dwords apart, so that the distinct rows one read touches sit in
+    // different banks
+    constexpr int kQRows = NH * S + 1, kQBufs = INT4 ? 1 : 2, kZeroRow = NH * S, kQS = 80;
+    __shared__ __attribute__((aligned(16))) uint32_t qt_s[4][kQBufs][kQRows * kQS];
     // int4: per-wave rings filled by direct loads kDepth tiles ahead; a tile's key
     // slot is free once it is scored, its value slot after its value product, S
     // tiles later (its value scales are read by the super-tile's softmax)
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     const int c = l & 15, g = l >> 4;
     const int hrow = c < NH ? c : NH;
 #pragma unroll
-    for (int qb = 0; qb < kQBufs; ++qb) qt_s[w][qb][kZeroRow * 64 + l] = 0u;
+    for (int qb = 0; qb < kQBufs; ++qb) qt_s[w][qb][kZeroRow * kQS + l] = 0u;
     const uint32_t magic = 0x64006400u;
     const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
     const int t_last = t_begin + kTile * (n_tiles - 1);
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
         for (int h = 0; h < NH; ++h) {
             const float ta = fmaf(ang.x, qa[h], ang.y * qb[h]);
             const float tb = fmaf(ang.x, qb[h], -ang.y * qa[h]);
-            qt[(row0 + h) * 64 + l] = __builtin_bit_cast(uint32_t, pack2(ta, tb));
+            qt[(row0 + h) * kQS + l] = __builtin_bit_cast(uint32_t, pack2(ta, tb));
         }
         ang = cmul(ang, stp);
     };
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     auto scores = [&](const Tile& T, const uint32_t* qt, int row, floatx4* sacc, bool zero) __attribute__((always_inline)) {
         half8 bq[4];
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) bq[k2] = *reinterpret_cast<const half8*>(qt + row * 64 + 16 * k2 + 4 * g);
+        for (int k2 = 0; k2 < 4; ++k2) bq[k2] = *reinterpret_cast<const half8*>(qt + row * kQS + 16 * k2 + 4 * g);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             floatx4 acc[8];
