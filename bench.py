@@ -14,12 +14,14 @@ One step = the whole decode hot path for one new token:
 Inputs are resident in HBM before the timed region. Two cache replicas are
 used in turn so that consecutive steps do not re-read the same 537 MB from the
 256 MB last-level cache.
+The timed region holds the K steps and nothing else (no events inside it).
 
 Prints one JSON line: the metric, whole-step throughput (latent-cache bytes per
 second over the timed steps), the partials kernel's achieved bandwidth against
 the HBM peak (roofline: the kernel's average launch duration over 20
 back-to-back launches of the same workload; launches bracketed one by one in
-the timed steps also appear under detail, inflated by the event gaps), and the
+an untimed diagnostic pass also appear under detail, inflated by the event
+gaps), and the
 float64 oracle timed on the host (cpu_baseline).
 """
 from __future__ import annotations
@@ -144,6 +146,25 @@ def measure_rows(torch, lrkv, dev, iters: int = 20) -> dict:
     ms = _time(torch, lambda: lrkv.decode_attn(lrkv.MODE_ABSORBED, c.desc, qa, None, None, 0.0, out, ws, Tq), iters)
     rows["absorbed_int4_B16_T16384"] = _row(ms, Bq * U * Tq * 2 * (R // 2 + 2 * R // 32), Bq * U * Tq * 4 * S * R)
     del c, qa, ws, out
+
+    # the RoPE path of the same layer at the sweep's shorter lengths (B = 1, one
+    # decode_attn call: prepare, partials, merge); T = 64K is the main line
+    g.manual_seed(7)
+    Ts = 32768
+    c = lrkv.LatentCache(1, U, S, GQ, DH, R, Ts, lrkv.FMT_FP16, THETA, device=dev)
+    c.hk.copy_((torch.randn(c.hk.shape, generator=g, device=dev) * sq).half())
+    c.hv.copy_((torch.randn(c.hv.shape, generator=g, device=dev) * sq[:, None]).half())
+    q2 = torch.randn((1, U * S * GQ, DH), generator=g, device=dev)
+    bk2 = (torch.randn((U, R, S * DH), generator=g, device=dev) / 16.0).half()
+    out = torch.empty((1, U * S * GQ, R), dtype=torch.float32, device=dev)
+    for Tn in (4096, 16384, 32768):
+        c.lens.fill_(Tn)
+        c.host_lens[:] = Tn
+        ws = c.workspace(lrkv.MODE_ROPE_RECON)
+        ms = _time(torch, lambda: lrkv.decode_attn(lrkv.MODE_ROPE_RECON, c.desc, q2, bk2, None, 0.0, out, ws, Tn),
+                   iters)
+        rows[f"rope_fp16_B1_T{Tn}"] = _row(ms, U * Tn * BYTES_PER_UNIT_TOKEN, U * Tn * FLOP_PER_UNIT_TOKEN)
+    del c, ws, out, q2, bk2
 
     # the projections on either side of the path (Llama-2-7B layer): latents of K and V
     # for a new token of every sequence (one call, 16 units of rank 256, d 4096) and
@@ -379,11 +400,8 @@ def main() -> int:
         return L
 
     mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    # timed region: K whole steps; the only events inside bracket the partials
-    # kernel of every EVERY-th step (each recorded event costs the GPU a few
-    # microseconds, so sampling keeps that cost out of most steps)
-    EVERY = 4
-    pev = [mk(2) if k % EVERY == 0 else None for k in range(K)]
+    # timed region: K whole steps, no events inside (a recorded event costs the
+    # GPU several microseconds)
     t_start, t_end = mk(2)
     log(f"bench: {W} warmup + {K} timed steps, {NR} cache replicas")
     for i in range(W):
@@ -391,18 +409,18 @@ def main() -> int:
     torch.cuda.synchronize()
     t_start.record()
     h0 = time.perf_counter()
-    lens_timed = [step(W + k, pev[k]) for k in range(K)]
+    lens_timed = [step(W + k) for k in range(K)]
     host_us = (time.perf_counter() - h0) / K * 1e6
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    part_each = np.array([e[0].elapsed_time(e[1]) for e in pev if e is not None])
     # untimed diagnostic pass: every phase bracketed by events
     dev_ev = [mk(5) for _ in range(D)]
     for k in range(D):
         step(W + K + k, dev_ev[k])
     torch.cuda.synchronize()
     ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in dev_ev])
+    part_each = ph[:, 2]           # the partials kernel of each diagnostic step
     # the kernel's average launch duration: NB back-to-back partials launches of the
     # timed workload (the replicas in turn, at their current lengths), one event
     # pair around the batch, so that no per-launch event gap enters the average
