@@ -372,7 +372,6 @@ int32_t lrkv_prefill_attn(const lrkv_latent_cache* c, const float* q, const void
     if (rc != LRKV_OK) return rc;
     if (!q || !bk || !p0 || !out || !aligned16(out) || !aligned16(q)) return LRKV_ERR_INVALID_ARG;
     if (!isfinite(sm_scale)) return LRKV_ERR_INVALID_ARG;
-    const int Hq = c->units * c->kv_per_unit * c->q_per_kv;
     const int n_tiles = (host_max_len + kTile - 1) / kTile;
     if (!workspace || ws_bytes < prefill_workspace_bytes(c->batch, c->units, c->kv_per_unit, c->q_per_kv, m_tokens,
                                                           c->head_dim, c->rank, n_tiles))

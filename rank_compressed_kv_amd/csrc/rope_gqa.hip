@@ -97,11 +97,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ void buf_dma16_lanes(int32x4 rsrc, uint32_t voff, const void* lds, uint64_t mask) {
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
     uint64_t save;
-    asm volatile("s_mov_b64 %0, exec\n\ts_and_b64 exec, exec, %4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+    // M0 (the LDS base) is an input bound to that register; the s_nop separates
+    // the compiler's write of it from the load
+    asm volatile("s_mov_b64 %0, exec\n\ts_and_b64 exec, exec, %4\n\ts_nop 0\n\t"
                  "buffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b64 exec, %0"
                  : "=&s"(save)
-                 : "v"(voff), "s"(rsrc), "s"(m), "s"(mask)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(rsrc), "{m0}"(m), "s"(mask)
+                 : "memory");
 }
 
 // v_permlane32_swap: upper 32 lanes of a <-> lower 32 lanes of b.

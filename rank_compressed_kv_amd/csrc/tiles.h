@@ -53,8 +53,8 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // `dst` must be wave-uniform; M0 carries its LDS byte address.
 __device__ __forceinline__ void dma16_async(const void* src, const void* dst) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds), "v"(src) : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "{m0}"(lds), "v"(src) : "memory");
 }
 
 // Raw buffer resource over [base, base + bytes): loads at or past `bytes` read
@@ -76,8 +76,10 @@ __device__ __forceinline__ int32x4 make_rsrc(const void* base, uint32_t bytes) {
 // wave-uniform. No immediate or scalar offset (zero on this path).
 __device__ __forceinline__ void buf_dma16(int32x4 rsrc, uint32_t voff, const void* lds) {
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(m) : "memory", "m0");
+    // M0 (the LDS base) is an input bound to that register, so the compiler sets
+    // it and knows it in use; the s_nop separates that write from the load
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "{m0}"(m) : "memory");
 }
 
 // ---------------------------------------------------------------- key tile, register staging
