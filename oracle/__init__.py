@@ -30,7 +30,8 @@ Modules and what pins each one (tests/test_oracle_*.py):
                  print for Qwen3-32B and Llama-3.1-8B.
 * ``brute``      pure-Python loop versions for tiny shapes.
 
-Parity unpinned: the pages print no worked numeric example of an attention
-output or of an int4 code, so end-to-end attention values are pinned only by
-the identities, special cases and brute force listed above.
+Every function above has at least one such pin. The pages print no worked
+numeric example of an attention output or of an int4 code, so those values are
+pinned by the identities, closed forms, special cases and brute force listed
+above rather than by stored printed numbers.
 """
