@@ -42,8 +42,3 @@ def palu_decode_one(hk: list, hv: list, Bk: list, q: list, col0: int, d_h: int,
         K.append(rope_vec(k, t, theta))
     qr = rope_vec(q, q_pos, theta)
     return attention(qr, K, hv, scale)
-
-
-def matmul(A: list, B: list) -> list:
-    return [[sum(A[i][k] * B[k][j] for k in range(len(B))) for j in range(len(B[0]))]
-            for i in range(len(A))]
