@@ -52,19 +52,25 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "rank_compressed_kv_amd", "csrc", "rope_decode.hip")
+# the partials kernel's source and the headers it compiles in; their digest keys the
+# recorded counter traffic
+KERNEL_SOURCES = [os.path.join(ROOT, "rank_compressed_kv_amd", "csrc", f)
+                  for f in ("rope_decode.hip", "tiles.h", "common.h")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "rope_decode_fw_llama2_7b_T65536.md")
 
 
 def recorded_traffic():
     """HBM bytes per launch of the partials kernel from the committed counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the kernel
-    source has changed since they were taken."""
+    source or a header it includes has changed since they were taken."""
     import hashlib
     import re
     try:
         text = open(TRAFFIC_RECORD).read()
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(f, "rb").read())
+        src = h.hexdigest()
     except OSError:
         return None
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
