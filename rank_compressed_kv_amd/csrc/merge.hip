@@ -14,13 +14,20 @@ namespace {
 // go through LDS, reductions are wave-wide shuffles.
 __global__ __launch_bounds__(64) void merge_splits(const float* __restrict__ part,
                                                    float* __restrict__ out, int n_split, int D) {
-    __shared__ float wts[1024];
+    constexpr int kPre = 32;                   // chunks whose outputs are requested up front
+    __shared__ float wts[1024], lsum[1024];
     const long bj = blockIdx.x;
     const int lane = threadIdx.x, d = blockIdx.y * 64 + lane;
     const float* pp = part + bj * n_split * (D + 2);
+    // one round trip for the common case: every chunk's (m, l) and the first kPre
+    // chunks' outputs are requested before any of them is used
+    float ov[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) ov[k] = (k < n_split && d < D) ? pp[(long)k * (D + 2) + 2 + d] : 0.0f;
     float mx = -INFINITY;
     for (int c = lane; c < n_split; c += 64) {
         const float m = pp[(long)c * (D + 2)];
+        lsum[c] = pp[(long)c * (D + 2) + 1];
         wts[c] = m;
         mx = fmaxf(mx, m);
     }
@@ -31,14 +38,22 @@ __global__ __launch_bounds__(64) void merge_splits(const float* __restrict__ par
         const float m = wts[c];
         const float wgt = m == -INFINITY ? 0.0f : exp2f(m - mx);
         wts[c] = wgt;
-        den = fmaf(wgt, pp[(long)c * (D + 2) + 1], den);
+        den = fmaf(wgt, lsum[c], den);
     }
     den = reduce_sum_width<64>(den);
     __syncthreads();
     if (d >= D) return;
     const float rden = 1.0f / den;
     float n0 = 0.0f, n1 = 0.0f, n2 = 0.0f, n3 = 0.0f;
-    int c = 0;
+#pragma unroll
+    for (int k = 0; k < kPre; k += 4) {
+        // chunks past n_split have ov = 0 (their weights are never read)
+        if (k < n_split) n0 = fmaf(wts[k], ov[k], n0);
+        if (k + 1 < n_split) n1 = fmaf(wts[k + 1], ov[k + 1], n1);
+        if (k + 2 < n_split) n2 = fmaf(wts[k + 2], ov[k + 2], n2);
+        if (k + 3 < n_split) n3 = fmaf(wts[k + 3], ov[k + 3], n3);
+    }
+    int c = kPre;
     for (; c + 4 <= n_split; c += 4) {
         n0 = fmaf(wts[c], pp[(long)c * (D + 2) + 2 + d], n0);
         n1 = fmaf(wts[c + 1], pp[(long)(c + 1) * (D + 2) + 2 + d], n1);
