@@ -12,8 +12,9 @@
  *    folded into W^o offline, so the output stays in latent space: o = p H^v.
  *    Without RoPE, B^k is absorbed into the query (q' = q (B^k)^T) and the
  *    scores are H^k q'. The Hadamard fold (A R)(R^T B) lets the latents be
- *    stored as int4 (per-token groups of 32, see the Supplementary details of the Palu digest and
- *    section 5 of the Shard post for the symmetric [-7, 7] range).
+ *    stored as int4 (per-token groups of 32, see the Supplementary details of
+ *    the Palu digest, and section 5 of the Shard post for the symmetric [-7, 7]
+ *    range).
  *  - PuzzleKV: page-based low-rank decomposition for KV-cache compression,
  *    section 3.3. Dense sink / local-window pages plus per-page factors
  *    X_hat = L R (Eq. 2), obtained from the P x P Gram matrix; attention runs
@@ -120,9 +121,9 @@ typedef struct lrkv_latent_cache {
  *   rv          [batch][kv_heads][max_pages][head_dim][rank_v]           half  R_V^T
  *   page_table  [batch][kv_heads][max_pages]                             int32
  *
- * factor_fmt LRKV_FMT_INT4_G32 (PuzzleKV section 1 and 4: factors stored in
- * int4; ranks up to 16): lk/rk/lv hold the factors' codes in the element order
- * above and rv in rank quads, R_V^T as [rank_v/4][head_dim][4], two codes per
+ * factor_fmt LRKV_FMT_INT4_G32 (PuzzleKV, Abstract and the contributions list
+ * of section 1: per-factor INT4 quantisation; ranks up to 16): lk/rk/lv hold
+ * the factors' codes in the element order above and rv in rank quads, R_V^T as [rank_v/4][head_dim][4], two codes per
  * byte (element 2i in the low nibble); lk_s/rk_s/lv_s/rv_s hold one fp16
  * scale per 32 consecutive elements of one page's factor, [batch][kv_heads]
  * [max_pages][elements / 32], with the latent codec of lrkv_append_latent
@@ -172,6 +173,13 @@ size_t lrkv_decode_workspace_bytes(int32_t mode, const void *cache, int32_t host
  * Append n_new tokens to every sequence: token i of sequence b is written at
  * position lens[b] + i, then lens[b] += n_new.
  *
+ * Defined by: Palu digest, Method details (the cache holds the latents h = x A
+ * instead of the keys and values; the Hadamard fold (A R)(R^T B) and, in the
+ * Supplementary details, per-token quantisation groups) and the Shard post,
+ * section 5, step 4 (symmetric int4 codes in [-7, 7]); for the hybrid cache,
+ * PuzzleKV section 3.3, step 5 (a new key/value pair goes to the newest dense
+ * page).
+ *
  * Palu modes (cache = lrkv_latent_cache*): new_k, new_v are device float32
  * [batch][units][n_new][rank] latents h = x A (in the Hadamard-mixed basis for
  * int4 caches). fp16 caches store round-to-nearest-even fp16. int4 caches
@@ -189,13 +197,24 @@ size_t lrkv_decode_workspace_bytes(int32_t mode, const void *cache, int32_t host
  *
  * Errors: INVALID_ARG (null pointers, n_new < 1, bad shapes), UNSUPPORTED
  * (rank not a multiple of 32 for int4, unsupported sizes), CAPACITY
- * (host_max_len + n_new exceeds the capacity).
+ * (host_max_len + n_new exceeds the capacity). The capacity check uses the
+ * caller's host_max_len; should it be stale (below a device length), the
+ * kernels still write nothing at or past the capacity (or past max_pages in
+ * the hybrid cache): such tokens are dropped, although lens still advances.
  */
 int32_t lrkv_append_latent(int32_t mode, const void *cache, const void *new_k, const void *new_v,
                            int32_t n_new, int32_t host_max_len, void *stream);
 
 /*
  * Single-query decode attention for every sequence and query head.
+ *
+ * Defined by: Palu digest, Method details (K = H^k B^k rebuilt on chip, RoPE
+ * applied to the rebuilt keys before the query attends, B^v fused into W^o so
+ * that the output is o = p H^v; without RoPE, key fusion q' = q (B^k)^T and
+ * scores H^k q') and Background (multi-head attention); PuzzleKV section 3.2,
+ * Eq. 1 (softmax attention) and section 3.3, step 4 (attention over dense and
+ * factored pages, factored pages scored as (q R^T) L^T, partial results merged
+ * by online softmax).
  *
  * LRKV_MODE_ROPE_RECON: q device float32 [batch][Hq][head_dim], un-rotated;
  *   bk device fp16 [units][rank][kv_per_unit*head_dim] (B^k, or the
@@ -249,6 +268,12 @@ int32_t lrkv_merge_partials(int32_t mode, const void *cache, float *out, void *w
                             size_t ws_bytes, int32_t host_max_len, int32_t n_split, void *stream);
 
 /*
+ * Defined by: PuzzleKV section 3.3, Eq. 2 (a page X ~ L R with L = U_r, the
+ * top-r left singular vectors, and R = Sigma_r W_r^T) and the Gram route of the
+ * same section (the top-r eigenvectors of the P x P matrix X X^T are U_r, so
+ * R = U_r^T X), with step 5 (a page is factored once it is full and has left
+ * the local window); the truncation is the Eckart-Young optimum of section 3.2.
+ *
  * Factor pages of a hybrid cache: for each (b, kv_head, page) triple in
  * `pages` (device int32 [n_pages][3]) and for K and V separately, form the
  * Gram matrix G = X X^T of the P x head_dim page X, take its top-r eigenvectors

@@ -25,8 +25,8 @@ Readings (the pages are silent or cut off):
 * the value side of a factored page (the text stops after the key-side score)
   is (a_p L^V) R^V by associativity, never forming V_hat.
 * eigen-order is descending, ties broken towards the lower index.
-* int4 factors (PuzzleKV, contributions list and section 4, "per-factor INT4
-  quantisation"; no grouping or order is given): each factor of a page is
+* int4 factors (PuzzleKV, Abstract and the contributions list of section 1:
+  per-factor INT4 quantisation; no grouping or order is given): each factor of a page is
   quantised with the latent codec (symmetric codes in [-7, 7], one fp16 scale
   per 32 consecutive elements) in its stored element order: keys L [P][r] and
   R [r][d] row-major, values L^T [r][P] and R^T in rank quads [r/4][d][4]. L is

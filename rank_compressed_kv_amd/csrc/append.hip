@@ -3,8 +3,9 @@
 //
 // Palu digest, Method details: the cache holds per-token latents h = x A
 // instead of keys and values. PuzzleKV section 3.3, step 5: new key/value pairs
-// go to the newest dense page. The int4 rule (Shard section 5, symmetric
-// [-7, 7]; Palu digest, Supplementary details: per-token groups of 32) is documented in lrkv.h.
+// go to the newest dense page. The int4 rule (Shard post, section 5, step 4:
+// symmetric [-7, 7]; Palu digest, Supplementary details: per-token groups of
+// 32) is documented in lrkv.h.
 #include "common.h"
 
 namespace lrkv {
@@ -32,6 +33,7 @@ __global__ void append_fp16(const float* __restrict__ nk, const float* __restric
     const int u = (int)(rest % U);
     const int b = (int)(rest / U);
     const int pos = lens[b] + i;
+    if (pos >= cap) return;                  // stale host bound: never write past the capacity
     const long src = (((long)b * U + u) * n_new + i) * r + d8 * 8;
     const float4 k0 = *reinterpret_cast<const float4*>(nk + src);
     const float4 k1 = *reinterpret_cast<const float4*>(nk + src + 4);
@@ -66,6 +68,7 @@ __global__ __launch_bounds__(256) void append_fp16_small(const float* __restrict
         const int u = rest % U;
         const int b = rest / U;
         const int pos = lens[b] + i;
+        if (pos >= cap) continue;
         const long src = (((long)b * U + u) * n_new + i) * r + d8 * 8;
         const long bu = (long)b * U + u;
         half8 kh;
@@ -95,6 +98,7 @@ __global__ void append_int4_k(const float* __restrict__ nk, uint8_t* __restrict_
     const int u = (int)(rest % U);
     const int b = (int)(rest / U);
     const int pos = lens[b] + i;
+    if (pos >= cap) return;
     const float* x = nk + ((((long)b * U + u) * n_new + i) * r + g * 32);
     int codes[32];
     half_t s16;
@@ -136,7 +140,7 @@ __global__ void append_int4_v(const float* __restrict__ nv, uint8_t* __restrict_
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int pos = 2 * pair + h;
-        own[h] = pos >= len && pos < len + n_new;
+        own[h] = pos >= len && pos < len + n_new && pos < cap;
         if (own[h]) {
             half_t s16;
             quant_group(nv + ((bu * n_new + (pos - len)) * r + g * 32), codes[h], &s16);
@@ -175,6 +179,7 @@ __global__ void append_paged(const half_t* __restrict__ nk, const half_t* __rest
     const int b = (int)(rest / H);
     const int pos = lens[b] + i;
     const int p = pos / P;
+    if (p >= max_pages) return;              // stale host bound: never write past the table
     const long bh = (long)b * H + h;
     int32_t* entry = table + bh * max_pages + p;
     if (*entry >= 0) return;                 // factored already (prefill)

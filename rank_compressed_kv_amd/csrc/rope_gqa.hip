@@ -3,9 +3,11 @@
 //
 // Palu digest, Method details: keys are cached as latents and rebuilt on chip
 // as K = H^k B^k; RoPE is applied at each token's position before the query
-// attends, and the output stays in latent space (o = p H^v). Shard digest,
-// section 5.1 (RoPE) and 5.4 (int4 latents, Hadamard rotation folded into the
-// factors, one fp16 scale per 32 elements per token).
+// attends, and the output stays in latent space (o = p H^v). The int4 latents
+// follow the same digest: the Hadamard rotation folded into the factors as
+// (A R)(R^T B) (Method details) and per-token groups of 32 elements with one
+// scale each (Supplementary details); the symmetric [-7, 7] code range is the
+// Shard post's (section 5, step 4), whose step 1 states the rotate-half RoPE.
 //
 // With several query heads per KV head, rebuilding K once per tile costs
 // 2 r d_h FLOP per token, against 2 r d_h NH for scoring in a per-head rotated

@@ -345,6 +345,107 @@ def test_absorbed_poisoned_tail(fmt_name, B, T, cap, r, s):
     assert err.max() <= TOL, err.max()
 
 
+def _tile_records(scores, chunk_tiles):
+    """Per chunk of `chunk_tiles` 32-token tiles: the tile indices (within the chunk)
+    whose maximum score exceeds every earlier tile's of that chunk."""
+    tm = scores[: len(scores) // 32 * 32].reshape(-1, 32).max(axis=1)
+    out = []
+    for c in range(0, len(tm), chunk_tiles):
+        seg = tm[c:c + chunk_tiles]
+        run = np.maximum.accumulate(seg)
+        out.append((np.nonzero(seg[1:] > run[:-1])[0] + 1, len(seg)))
+    return out
+
+
+@pytest.mark.parametrize("fmt_name,r,s,n_split", [("fp16", 256, 4, 1), ("fp16", 256, 4, 3), ("int4", 256, 4, 1),
+                                                  ("int4", 256, 4, 2), ("int4", 64, 2, 1), ("fp16", 64, 2, 2)])
+def test_absorbed_many_tiles_per_wave(fmt_name, r, s, n_split):
+    """Each wave of the absorbed kernel walks tiles w, w + 4, ... of its chunk and
+    carries its running max, running sum and accumulators from tile to tile. A
+    forced small split count at T = 4096 gives every wave 8 to 32 tiles. The key
+    latents' amplitude grows along the sequence, so that in every chunk of
+    sequence 0 the running max moves at some tile past the first four (a record
+    over the whole chunk is also a record of the wave owning that tile: the
+    rescale of non-zero accumulators runs) and stays put at others (the
+    unchanged-max branch runs). Sequence 1 is ragged, ending inside a chunk."""
+    R = _R()
+    fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
+    B, T, U, dh = 2, 4096, 8, 128
+    say(f"absorbed many tiles per wave: {fmt_name} r={r} heads/unit={s} T={T} n_split={n_split}")
+    lay = synth.latent_layer(35, B, U, T, r, s * dh, 96.0)
+    hk = lay["hk"] * np.linspace(0.4, 1.6, T, dtype=np.float32)[None, None, :, None]
+    hv = lay["hv"]
+    qa = synth.queries(36, B, U * s, r, 3.0)
+    store = oattn.stored_fp16 if fmt == R.FMT_FP16 else oattn.stored_int4
+    sk, sv = store(hk), store(hv)
+    chunk_tiles = -(-(T // 32) // n_split)
+    for j in range(U * s):
+        for rec, n in _tile_records(sk[0, j // s] @ qa[0, j].astype(np.float64), chunk_tiles):
+            assert (rec >= 4).any() and len(rec) < n - 1, (j, rec)
+    cache = R.LatentCache(B, U, s, 1, dh, r, T, fmt, 0.0)
+    cache.append(to_dev(hk), to_dev(hv))
+    lens = np.array([T, T - 1013])
+    cache.lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    cache.host_lens[:] = lens
+    got = cache.decode(R.MODE_ABSORBED, to_dev(qa), n_split=n_split)
+    torch.cuda.synchronize()
+    ref = oattn.palu_decode_absorbed(sk, sv, qa, lens, s, 1, dh)
+    err = rel_l2(got.cpu().numpy(), ref)
+    say(f"  max rel-L2 {err.max():.3g}")
+    assert err.max() <= TOL, err.max()
+
+
+@pytest.mark.parametrize("fmt_name", ["fp16", "int4"])
+def test_absorbed_workload_sampled(fmt_name):
+    """The absorbed-query workload at full size in the launch configuration the
+    benchmark times: 16 sequences of 16K tokens, Llama-2-7B layer (8 units of 4
+    heads, rank 256); the default chunking gives each (sequence, unit) 8 chunks of
+    64 tiles, 16 tiles per wave. The cache is written on the device by torch from
+    a seeded generator (fp16 latents sqrt(s_i) z; int4: random codes in [-7, 7]
+    with decaying per-group scales); sampled (sequence, unit) pairs are read back
+    and all four heads of each checked against the oracle."""
+    R = _R()
+    fmt = R.FMT_FP16 if fmt_name == "fp16" else R.FMT_INT4_G32
+    B, T, U, s, r, dh = 16, 16384, 8, 4, 256, 128
+    say(f"absorbed workload sampled: {fmt_name} B={B} T={T}")
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(37)
+    cache = R.LatentCache(B, U, s, 1, dh, r, T, fmt, 0.0)
+    root = torch.exp(-torch.arange(r, device=dev, dtype=torch.float32) / (2 * 96.0))
+    if fmt == R.FMT_FP16:
+        cache.hk.copy_((torch.randn(cache.hk.shape, generator=g, device=dev) * root).half())
+        cache.hv.copy_((torch.randn(cache.hv.shape, generator=g, device=dev) * root[:, None]).half())
+    else:
+        for a in (cache.hk, cache.hv):
+            c = torch.randint(-7, 8, a.shape[:-1] + (2 * a.shape[-1],), generator=g, device=dev, dtype=torch.int16)
+            a.copy_(((c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)).to(torch.uint8))
+        grp = root[16::32] / 4.0                                   # one scale per 32 ranks, ~ the group's amax / 7
+        cache.sk.copy_((grp * (0.5 + torch.rand(cache.sk.shape, generator=g, device=dev))).half())
+        cache.sv.copy_((grp[:, None] * (0.5 + torch.rand(cache.sv.shape, generator=g, device=dev))).half())
+    cache.lens.fill_(T)
+    cache.host_lens[:] = T
+    qa = torch.randn((B, U * s, r), generator=g, device=dev) * 2.0
+    got = cache.decode(R.MODE_ABSORBED, qa)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.isfinite(got).all()
+    qn = qa.cpu().numpy()
+    for b, u in ((0, 0), (9, 3), (15, 7)):
+        if fmt == R.FMT_FP16:
+            hk = cache.hk[b:b + 1, u:u + 1].cpu().numpy().astype(np.float64)
+            hv = hv_fp16_tokens(cache.hv[b:b + 1, u:u + 1]).astype(np.float64)
+        else:
+            hk = hk_int4_codes(cache.hk[b:b + 1, u:u + 1]) * \
+                np.repeat(cache.sk[b:b + 1, u:u + 1].cpu().numpy().astype(np.float64), 32, axis=-1)
+            hv = hv_int4_codes(cache.hv[b:b + 1, u:u + 1]) * \
+                np.repeat(sv_tokens(cache.sv[b:b + 1, u:u + 1]).astype(np.float64), 32, axis=-1)
+        ref = oattn.palu_decode_absorbed(hk, hv, qn[b:b + 1, u * s:(u + 1) * s], [T], s, 1, dh)
+        err = rel_l2(got[b, u * s:(u + 1) * s], ref[0]).max()
+        say(f"  (b={b}, u={u}) max rel-L2 {err:.3g}")
+        assert err <= TOL, ((b, u), err)
+
+
 # ----------------------------------------------------------------------------- full size, sampled
 
 def test_rope_full_size_sampled():

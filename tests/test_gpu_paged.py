@@ -28,6 +28,13 @@ def _R():
     return R
 
 
+def _oracle(q, T, dk, dv, Lk, Rk, Lv, Rv, sink, window, G):
+    """The oracle's hybrid decode in its plain form: every factored page rebuilt as
+    L R, all pages concatenated, textbook softmax attention."""
+    lens = [T] * q.shape[0] if np.isscalar(T) else T
+    return opaged.hybrid_decode(q, lens, dk, dv, Lk, Rk, Lv, Rv, P, sink, window, G, form="reconstruct")
+
+
 def _oracle_factors(dense, r):
     """Oracle page factors (truncated SVD) of every full page: [B][H][npg][P][r], [..][r][d]."""
     B, H, T, d = dense.shape
@@ -91,7 +98,7 @@ def test_hybrid_decode_parity(B, H, G, T, rk, rv):
     q = synth.queries(54, B, H * G, 128, 2.0)
     got = cache.decode(to_dev(q))
     torch.cuda.synchronize()
-    ref = opaged.hybrid_decode(q, [T] * B, dense["k"], dense["v"], Lk, Rk, Lv, Rv, P, 1, 4, G)
+    ref = _oracle(q, T, dense["k"], dense["v"], Lk, Rk, Lv, Rv, 1, 4, G)
     err = rel_l2(got.cpu().numpy(), ref)
     assert err.max() <= TOL, err.max()
 
@@ -174,23 +181,88 @@ def test_decode_loop_against_oracle():
         if i % 27 == 0 or i == steps - 1:
             q = synth.queries(100 + i, B, H * G, 128, 2.0)
             got = cache.decode(to_dev(q)).cpu().numpy()
-            ref = opaged.hybrid_decode(q, [T] * B, dense["k"], dense["v"], Lk, Rk, Lv, Rv, P, 1, 4, G)
+            ref = _oracle(q, T, dense["k"], dense["v"], Lk, Rk, Lv, Rv, 1, 4, G)
             assert rel_l2(got, ref).max() <= TOL, (T, rel_l2(got, ref).max())
 
 
-def test_hybrid_split_independence():
+@pytest.mark.parametrize("T", [32 * 128, 32 * 128 + 19])
+def test_hybrid_split_independence(T):
+    """Every split count checked against the oracle (plain reconstruct form) and
+    against each other. n_split = 1 is raised to the fewest chunks of at most 64
+    pages, so one wave walks 64 pages (43 at T = 4115) and uses every bit of its
+    factored / dense page masks."""
     R = _R()
-    B, H, G, T = 1, 2, 4, 32 * 40
-    say("hybrid split independence")
-    cache = R.PagedCache(B, H, G, 128, P, 1, 4, 12, 12, max_pages=48)
+    B, H, G, rk, rv = 1, 2, 4, 12, 12
+    say(f"hybrid split independence: T={T}, n_split 1/5/40/auto")
+    npg = (T + P - 1) // P
+    cache = R.PagedCache(B, H, G, 128, P, 1, 4, rk, rv, max_pages=npg + 2)
     dense = synth.paged_dense(59, B, H, T, 128)
-    cache.prefill(to_dev(dense["k"]), to_dev(dense["v"]))
-    q = to_dev(synth.queries(60, B, H * G, 128, 2.0))
+    fk = synth.factored_pages(62, B * H * npg, P, 128, rk)
+    fv = synth.factored_pages(63, B * H * npg, P, 128, rv)
+    shp = lambda a, last: a.reshape((B, H, npg) + last)
+    Lk, Rk = shp(fk["L"], (P, rk)), shp(fk["R"], (rk, 128))
+    Lv, Rv = shp(fv["L"], (P, rv)), shp(fv["R"], (rv, 128))
+    _write_cache_directly(cache, dense["k"], dense["v"], Lk, Rk, Lv, Rv, T)
+    qh = synth.queries(60, B, H * G, 128, 2.0)
+    q = to_dev(qh)
     outs = [cache.decode(q, n_split=n).cpu().numpy() for n in (1, 5, 40, 0)]
+    ref = _oracle(qh, T, dense["k"], dense["v"], Lk, Rk, Lv, Rv, 1, 4, G)
+    for o in outs:
+        assert rel_l2(o, ref).max() <= TOL, rel_l2(o, ref).max()
     # p and w = p L_V enter the value products in fp16, rounded relative to each
     # chunk's own running max, so chunkings differ by a few fp16 roundings
     for o in outs[1:]:
         assert rel_l2(o, outs[0]).max() <= 2 * 2.0 ** -11
+
+
+@pytest.mark.parametrize("n_split", [0, 32])
+def test_hybrid_workload_full_sampled(n_split):
+    """The hybrid decode at the workload's full size (8 sequences x 8 KV heads x 32K
+    tokens, P = 32, 1 sink + 4 window pages, rank 12, fp16 factors) in the launch
+    configuration the benchmark times (default chunking: 16 chunks of 64 pages per
+    (sequence, KV head), so each wave uses all 64 bits of its page masks), and
+    with 32 chunks of 32 pages. Factors and dense pages are
+    written on the device by torch from a seeded generator (L entries of size
+    1/sqrt(P), R entries of size 3); sampled (sequence, KV head) pairs are read
+    back and checked against the oracle's plain reconstruct form."""
+    R = _R()
+    B, H, G, T, rk = 8, 8, 4, 32768, 12
+    say(f"hybrid workload full sampled: fp16 factors B={B} H={H} T={T} n_split={n_split}")
+    dev = torch.device("cuda")
+    cache = R.PagedCache(B, H, G, 128, P, 1, 4, rk, rk, max_pages=T // P + 8)
+    g = torch.Generator(device=dev)
+    g.manual_seed(90)
+    npg = T // P
+    expect = opaged.page_table(T, P, 1, 4)
+    cache.page_table[:, :, :npg] = torch.from_numpy(expect).to(dev)
+    cache.lens.fill_(T)
+    cache.host_lens[:] = T
+    for n, sd in (("lk", P ** -0.5), ("rk", 3.0), ("lv", P ** -0.5), ("rv", 3.0)):
+        a = getattr(cache, n)
+        a.copy_((torch.randn(a.shape, generator=g, device=dev) * sd).half())
+    cache.dense_k.copy_(torch.randn(cache.dense_k.shape, generator=g, device=dev).half())
+    cache.dense_v.copy_(torch.randn(cache.dense_v.shape, generator=g, device=dev).half())
+    q = torch.randn((B, H * G, 128), generator=g, device=dev)
+    got = cache.decode(q, n_split=n_split).cpu().numpy()
+    assert np.isfinite(got).all()
+    qn = q.cpu().numpy().astype(np.float64)
+    for (b, h) in ((0, 0), (3, 6), (7, 7)):
+        lk = cache.lk[b, h, :npg].cpu().numpy().astype(np.float64)[None, None]
+        rk_ = cache.rk[b, h, :npg].cpu().numpy().astype(np.float64)[None, None]
+        lv = np.swapaxes(cache.lv[b, h, :npg].cpu().numpy().astype(np.float64), -1, -2)[None, None]
+        rv = np.swapaxes(cache.rv[b, h, :npg].cpu().numpy().astype(np.float64), -1, -2)[None, None]
+        dk = np.zeros((1, 1, T, 128))
+        dv = np.zeros((1, 1, T, 128))
+        dks = cache.dense_k[b, h].cpu().numpy().astype(np.float64)
+        dvs = np.swapaxes(cache.dense_v[b, h].cpu().numpy().astype(np.float64), -1, -2)
+        for p in np.nonzero(expect < 0)[0]:
+            slot = -1 - expect[p]
+            dk[0, 0, p * P:(p + 1) * P] = dks[slot]
+            dv[0, 0, p * P:(p + 1) * P] = dvs[slot]
+        ref = _oracle(qn[b:b + 1, h * G:(h + 1) * G], T, dk, dv, lk, rk_, lv, rv, 1, 4, G)
+        err = rel_l2(got[b, h * G:(h + 1) * G], ref[0]).max()
+        say(f"  (b={b}, h={h}) max rel-L2 {err:.3g}")
+        assert err <= TOL, ((b, h), err)
 
 
 def test_hybrid_workload_sampled():
@@ -208,8 +280,7 @@ def test_hybrid_workload_sampled():
         sub = lambda a: a[b:b + 1, h:h + 1]
         Lk, Rk = _oracle_factors(sub(dense["k"]), 12)
         Lv, Rv = _oracle_factors(sub(dense["v"]), 12)
-        ref = opaged.hybrid_decode(q[b:b + 1, h * G:(h + 1) * G], [T], sub(dense["k"]), sub(dense["v"]),
-                                   Lk, Rk, Lv, Rv, P, 1, 4, G)
+        ref = _oracle(q[b:b + 1, h * G:(h + 1) * G], T, sub(dense["k"]), sub(dense["v"]), Lk, Rk, Lv, Rv, 1, 4, G)
         assert rel_l2(got[b, h * G:(h + 1) * G], ref[0]).max() <= TOL
 
 
@@ -310,7 +381,7 @@ def test_hybrid_int4_decode_parity(B, H, G, T, rk, rv):
     q = synth.queries(74, B, H * G, 128, 2.0)
     got = cache.decode(to_dev(q))
     torch.cuda.synchronize()
-    ref = opaged.hybrid_decode(q, [T] * B, dense["k"], dense["v"], Lk, Rk, Lv, Rv, P, 1, 4, G)
+    ref = _oracle(q, T, dense["k"], dense["v"], Lk, Rk, Lv, Rv, 1, 4, G)
     err = rel_l2(got.cpu().numpy(), ref)
     assert err.max() <= TOL, err.max()
 
@@ -393,7 +464,7 @@ def test_int4_decode_loop_end_to_end():
     got = cache.decode(to_dev(q)).cpu().numpy()
     Lk, Rk = _oracle_factors(dense["k"][:, :, :T], rank)
     Lv, Rv = _oracle_factors(dense["v"][:, :, :T], rank)
-    exact = opaged.hybrid_decode(q, [T] * B, dense["k"], dense["v"], Lk, Rk, Lv, Rv, P, 1, 4, G)
+    exact = _oracle(q, T, dense["k"], dense["v"], Lk, Rk, Lv, Rv, 1, 4, G)
     q4 = [np.zeros_like(a) for a in (Lk, Rk, Lv, Rv)]
     for b in range(B):
         for h in range(H):
@@ -401,7 +472,7 @@ def test_int4_decode_loop_end_to_end():
                 for X, side, i in ((dense["k"], "key", 0), (dense["v"], "value", 2)):
                     L_hat, R_hat, _, _ = opaged.factor_int4(X[b, h, p * P:(p + 1) * P], rank, side)
                     q4[i][b, h, p], q4[i + 1][b, h, p] = L_hat, R_hat
-    ref4 = opaged.hybrid_decode(q, [T] * B, dense["k"], dense["v"], *q4, P, 1, 4, G)
+    ref4 = _oracle(q, T, dense["k"], dense["v"], *q4, 1, 4, G)
     e_oracle = rel_l2(ref4, exact).max()
     e_gpu = rel_l2(got, exact).max()
     say(f"  int4 error vs exact rank-r attention: gpu {e_gpu:.3e}, oracle {e_oracle:.3e}")
@@ -426,31 +497,46 @@ def test_hybrid_int4_sink_window_geometry():
     Lk, Rk, Lv, Rv = _write_int4_cache(cache, dense["k"], dense["v"], Lk, Rk, Lv, Rv, T)
     q = synth.queries(84, B, H * G, 128, 2.0)
     got = cache.decode(to_dev(q)).cpu().numpy()
-    ref = opaged.hybrid_decode(q, [T] * B, dense["k"], dense["v"], Lk, Rk, Lv, Rv, P, 2, 3, G)
+    ref = _oracle(q, T, dense["k"], dense["v"], Lk, Rk, Lv, Rv, 2, 3, G)
     assert rel_l2(got, ref).max() <= TOL
 
 
-def test_hybrid_int4_split_independence():
+@pytest.mark.parametrize("T", [32 * 128, 32 * 70 + 5])
+def test_hybrid_int4_split_independence(T):
+    """int4 factors (oracle-quantised): every split count against the oracle and
+    against each other; n_split = 1 gives one wave up to 64 pages."""
     R = _R()
-    B, H, G, T = 1, 2, 4, 32 * 40
-    say("hybrid int4 split independence")
-    cache = R.PagedCache(B, H, G, 128, P, 1, 4, 12, 12, max_pages=48, factor_fmt=R.FMT_INT4_G32)
+    B, H, G, rk, rv = 1, 2, 4, 12, 12
+    say(f"hybrid int4 split independence: T={T}, n_split 1/5/40/auto")
+    npg = (T + P - 1) // P
+    cache = R.PagedCache(B, H, G, 128, P, 1, 4, rk, rv, max_pages=npg + 2, factor_fmt=R.FMT_INT4_G32)
     dense = synth.paged_dense(78, B, H, T, 128)
-    cache.prefill(to_dev(dense["k"]), to_dev(dense["v"]))
-    q = to_dev(synth.queries(79, B, H * G, 128, 2.0))
+    fk = synth.factored_pages(85, B * H * npg, P, 128, rk)
+    fv = synth.factored_pages(86, B * H * npg, P, 128, rv)
+    shp = lambda a, last: a.reshape((B, H, npg) + last).astype(np.float64)
+    Lk, Rk = shp(fk["L"], (P, rk)), shp(fk["R"], (rk, 128))
+    Lv, Rv = shp(fv["L"], (P, rv)), shp(fv["R"], (rv, 128))
+    Lk, Rk, Lv, Rv = _write_int4_cache(cache, dense["k"], dense["v"], Lk, Rk, Lv, Rv, T)
+    qh = synth.queries(79, B, H * G, 128, 2.0)
+    q = to_dev(qh)
     outs = [cache.decode(q, n_split=n).cpu().numpy() for n in (1, 5, 40, 0)]
+    ref = _oracle(qh, T, dense["k"], dense["v"], Lk, Rk, Lv, Rv, 1, 4, G)
+    for o in outs:
+        assert rel_l2(o, ref).max() <= TOL, rel_l2(o, ref).max()
     for o in outs[1:]:
         assert rel_l2(o, outs[0]).max() <= 2 * 2.0 ** -11
 
 
-def test_hybrid_int4_workload_sampled():
+@pytest.mark.parametrize("n_split", [0, 16])
+def test_hybrid_int4_workload_sampled(n_split):
     """The int4 hybrid decode at the workload's full size (8 sequences x 8 KV heads x
     32K tokens, P=32, 1 sink, 4 window, rank 12), in the launch configuration the
-    benchmark times: random int4 factor codes in [-7, 7] and fp16 scales, dense pages
-    from a seeded generator; sampled (sequence, KV head) pairs against the oracle."""
+    benchmark times (32 pages per wave), and with 16 chunks (64 pages per wave):
+    random int4 factor codes in [-7, 7] and fp16 scales, dense pages from a seeded
+    generator; sampled (sequence, KV head) pairs against the oracle."""
     R = _R()
     B, H, G, T, rk = 8, 8, 4, 32768, 12
-    say(f"hybrid int4 workload sampled: B={B} H={H} T={T}")
+    say(f"hybrid int4 workload sampled: B={B} H={H} T={T} n_split={n_split}")
     dev = torch.device("cuda")
     cache = R.PagedCache(B, H, G, 128, P, 1, 4, rk, rk, max_pages=T // P + 8, factor_fmt=R.FMT_INT4_G32)
     g = torch.Generator(device=dev)
@@ -471,7 +557,7 @@ def test_hybrid_int4_workload_sampled():
     cache.dense_k.copy_(torch.randn(cache.dense_k.shape, generator=g, device=dev).half())
     cache.dense_v.copy_(torch.randn(cache.dense_v.shape, generator=g, device=dev).half())
     q = torch.randn((B, H * G, 128), generator=g, device=dev)
-    got = cache.decode(q).cpu().numpy()
+    got = cache.decode(q, n_split=n_split).cpu().numpy()
     qn = q.cpu().numpy().astype(np.float64)
     for (b, h) in ((0, 0), (5, 3), (7, 7)):
         dec = {}
@@ -486,7 +572,7 @@ def test_hybrid_int4_workload_sampled():
             slot = -1 - expect[p]
             dk[0, 0, p * P:(p + 1) * P] = dks[slot]
             dv[0, 0, p * P:(p + 1) * P] = dvs[slot]
-        ref = opaged.hybrid_decode(qn[b:b + 1, h * G:(h + 1) * G], [T], dk, dv, dec["lk"], dec["rk"],
-                                   dec["lv"], dec["rv"], P, 1, 4, G)
+        ref = _oracle(qn[b:b + 1, h * G:(h + 1) * G], T, dk, dv, dec["lk"], dec["rk"], dec["lv"], dec["rv"],
+                      1, 4, G)
         err = rel_l2(got[b, h * G:(h + 1) * G], ref[0]).max()
         assert err <= TOL, ((b, h), err)
