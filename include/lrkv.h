@@ -24,7 +24,8 @@
  * Conventions for every entry point:
  *  - Ownership: the caller owns every buffer (device memory, e.g. PyTorch
  *    tensors). The library allocates nothing; scratch memory is the caller's
- *    `workspace`, sized by lrkv_decode_workspace_bytes.
+ *    `workspace`, sized by lrkv_decode_workspace_bytes (lrkv_decode_attn_noalloc
+ *    uses a static device array instead).
  *  - Pointers marked "device" must be device memory of the current HIP device.
  *  - Asynchrony: calls only enqueue kernels on `stream` (a hipStream_t; NULL is
  *    the default stream) and never synchronise. Results are ready when the
@@ -34,7 +35,8 @@
  *    untouched. A failed kernel launch returns LRKV_ERR_HIP. No C++ exception
  *    crosses the ABI.
  *  - Thread safety: calls are re-entrant; the library keeps no global state
- *    beyond its loaded code objects.
+ *    beyond its loaded code objects, except the static scratch array of
+ *    lrkv_decode_attn_noalloc and its per-device address.
  *  - Lengths: `lens` (device, int32 [batch]) holds each sequence's current
  *    number of cached tokens; `host_max_len` is the caller's host-side bound on
  *    max(lens) (used for capacity checks and grid sizing; it must not be
@@ -56,7 +58,9 @@ typedef enum {
     LRKV_ERR_UNSUPPORTED = -2,   /* valid but not compiled: rank / head_dim / groups */
     LRKV_ERR_CAPACITY = -3,      /* the append would overflow the cache              */
     LRKV_ERR_WORKSPACE = -4,     /* workspace missing or too small                   */
-    LRKV_ERR_HIP = -5            /* a HIP call failed                                */
+    LRKV_ERR_HIP = -5,           /* a HIP call failed                                */
+    LRKV_ERR_SCRATCH = -6        /* more than lrkv_decode_attn_noalloc's static
+                                    scratch (LRKV_NOALLOC_SCRATCH_BYTES) needed      */
 } lrkv_status;
 
 typedef enum {
@@ -238,6 +242,33 @@ int32_t lrkv_append_latent(int32_t mode, const void *cache, const void *new_k, c
 int32_t lrkv_decode_attn(int32_t mode, const void *cache, const float *q, const void *bk,
                          const int32_t *q_pos, float sm_scale, float *out, void *workspace,
                          size_t ws_bytes, int32_t host_max_len, int32_t n_split, void *stream);
+
+/*
+ * lrkv_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same validation, kernels and result as lrkv_decode_attn with the same
+ * arguments, but the workspace is a static device array of
+ * LRKV_NOALLOC_SCRATCH_BYTES inside the library instead of a caller buffer.
+ * The caller still passes the cache, q, bk, q_pos and out; the call performs no
+ * allocation of any kind.
+ *
+ * Each device the library runs on holds its own copy of the array until the
+ * process ends; its address is looked up once per device, on the first call
+ * made with that device current. The array keeps the last call's contents
+ * (nothing in it needs clearing between calls). All calls on one device share
+ * it, so two calls whose executions overlap on that device (different streams,
+ * or host threads without ordering) race and give undefined results: order
+ * them on one stream.
+ *
+ * Errors: as lrkv_decode_attn, except that a call whose workspace
+ * (lrkv_decode_workspace_bytes for the same arguments) exceeds
+ * LRKV_NOALLOC_SCRATCH_BYTES returns LRKV_ERR_SCRATCH before anything is
+ * enqueued; LRKV_ERR_HIP if the array's address cannot be obtained.
+ */
+#define LRKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t lrkv_decode_attn_noalloc(int32_t mode, const void *cache, const float *q, const void *bk,
+                                 const int32_t *q_pos, float sm_scale, float *out,
+                                 int32_t host_max_len, int32_t n_split, void *stream);
 
 /*
  * The three steps lrkv_decode_attn enqueues, callable one by one with the same

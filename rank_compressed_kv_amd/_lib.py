@@ -14,6 +14,9 @@ LRKV_ERR_UNSUPPORTED = -2
 LRKV_ERR_CAPACITY = -3
 LRKV_ERR_WORKSPACE = -4
 LRKV_ERR_HIP = -5
+LRKV_ERR_SCRATCH = -6
+
+NOALLOC_SCRATCH_BYTES = 16 << 20      # LRKV_NOALLOC_SCRATCH_BYTES
 
 FMT_FP16 = 0
 FMT_INT4_G32 = 1
@@ -30,6 +33,7 @@ EXPORTS = (
     "lrkv_decode_attn", "lrkv_decode_prepare", "lrkv_decode_partials", "lrkv_merge_partials",
     "lrkv_factor_page", "lrkv_paged_plan", "lrkv_project_workspace_bytes", "lrkv_latent_project",
     "lrkv_output_project", "lrkv_probe_stream_read", "lrkv_prefill_workspace_bytes", "lrkv_prefill_attn",
+    "lrkv_decode_attn_noalloc",
 )
 
 c_i32 = ctypes.c_int32
@@ -83,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.lrkv_decode_attn.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp,
                                        ctypes.c_size_t, c_i32, c_i32, c_vp]
         L.lrkv_decode_attn.restype = c_i32
+        L.lrkv_decode_attn_noalloc.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_i32, c_i32,
+                                               c_vp]
+        L.lrkv_decode_attn_noalloc.restype = c_i32
         L.lrkv_decode_prepare.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp,
                                           ctypes.c_size_t, c_i32, c_i32, c_vp]
         L.lrkv_decode_prepare.restype = c_i32

@@ -17,7 +17,8 @@ from ._lib import (BLOCK, FMT_FP16, FMT_INT4_G32, MODE_ABSORBED, MODE_HYBRID_PAG
                    MODE_ROPE_RECON, PAGE_EMPTY, LatentCacheDesc, PagedCacheDesc, LrkvError)
 
 __all__ = [
-    "decode_workspace_bytes", "append_latent", "decode_attn", "decode_prepare", "decode_partials",
+    "decode_workspace_bytes", "append_latent", "decode_attn", "decode_attn_noalloc", "decode_prepare",
+    "decode_partials",
     "merge_partials", "factor_page", "paged_plan", "project_workspace_bytes", "latent_project",
     "output_project", "probe_stream_read",
     "LatentCache", "PagedCache", "LrkvError",
@@ -62,6 +63,14 @@ def decode_attn(mode: int, desc, q, bk, q_pos, sm_scale: float, out, workspace,
     L.check(L.lib().lrkv_decode_attn(mode, ctypes.byref(desc), _p(q), _p(bk), _p(q_pos),
                                      float(sm_scale), _p(out), _p(workspace), ws_bytes,
                                      host_max_len, n_split, _stream(stream)), "lrkv_decode_attn")
+
+
+def decode_attn_noalloc(mode: int, desc, q, bk, q_pos, sm_scale: float, out, host_max_len: int,
+                        n_split: int = 0, stream=None) -> None:
+    """lrkv_decode_attn with the library's static device scratch as its workspace."""
+    L.check(L.lib().lrkv_decode_attn_noalloc(mode, ctypes.byref(desc), _p(q), _p(bk), _p(q_pos),
+                                             float(sm_scale), _p(out), host_max_len, n_split,
+                                             _stream(stream)), "lrkv_decode_attn_noalloc")
 
 
 def _ws(workspace):

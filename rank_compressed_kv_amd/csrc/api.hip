@@ -158,6 +158,7 @@ const char* lrkv_status_string(int32_t s) {
         case LRKV_ERR_CAPACITY: return "cache capacity exceeded";
         case LRKV_ERR_WORKSPACE: return "workspace missing or too small";
         case LRKV_ERR_HIP: return "HIP error";
+        case LRKV_ERR_SCRATCH: return "call needs more than the no-allocation entry point's static scratch";
         default: return "unknown status";
     }
 }
@@ -204,11 +205,12 @@ int32_t lrkv_append_latent(int32_t mode, const void* cache, const void* new_k, c
 
 // Shared validation and dispatch of the decode entry points. `phases` selects
 // which of prepare / partials / merge are enqueued; the pointers each phase
-// needs are checked here.
-static int32_t decode_common(int32_t mode, int phases, const void* cache, const float* q,
+// needs are checked here. With `ws_need` non-null nothing is enqueued: after the
+// argument checks the workspace size the call needs is stored there.
+int32_t lrkv::decode_common(int32_t mode, int phases, const void* cache, const float* q,
                              const void* bk, const int32_t* q_pos, float sm_scale, float* out,
                              void* workspace, size_t ws_bytes, int32_t host_max_len, int32_t n_split,
-                             void* stream) {
+                             void* stream, size_t* ws_need) {
     if (!cache || host_max_len < 1) return LRKV_ERR_INVALID_ARG;
     if ((phases & kPhaseMerge) && !out) return LRKV_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
@@ -220,6 +222,10 @@ static int32_t decode_common(int32_t mode, int phases, const void* cache, const 
         if ((phases & kPhasePartials) && !q) return LRKV_ERR_INVALID_ARG;
         if (host_max_len > c->max_pages * c->page_size) return LRKV_ERR_INVALID_ARG;
         const PagedWorkspace w = paged_workspace(c, host_max_len, n_split);
+        if (ws_need) {
+            *ws_need = w.total;
+            return LRKV_OK;
+        }
         if (!workspace || ws_bytes < w.total || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
         const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
         return launch_decode_hybrid(phases, c, q, scale, out, workspace, w, st);
@@ -239,6 +245,10 @@ static int32_t decode_common(int32_t mode, int phases, const void* cache, const 
     if (g.r % 32) return LRKV_ERR_UNSUPPORTED;
     if (!latent_shape_supported(mode, g)) return LRKV_ERR_UNSUPPORTED;
     const LatentWorkspace w = latent_workspace(mode, g, host_max_len, n_split);
+    if (ws_need) {
+        *ws_need = w.total;
+        return LRKV_OK;
+    }
     if (!workspace || ws_bytes < w.total || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
     return launch_decode_latent(mode, phases, c, q, (const half_t*)bk, q_pos, scale, out, workspace,

@@ -118,6 +118,12 @@ constexpr int kPhasePrepare = 1, kPhasePartials = 2, kPhaseMerge = 4, kPhaseAll 
 constexpr int kQpRowMajor = 0, kQpFragments = 1, kQpGqaFragments = 2;
 bool use_gqa_kernel(const LatentGeom& g);
 
+// Validation and dispatch shared by every decode entry point (api.hip). With
+// ws_need non-null it only validates and stores the workspace size needed.
+int32_t decode_common(int32_t mode, int phases, const void* cache, const float* q, const void* bk,
+                      const int32_t* q_pos, float sm_scale, float* out, void* workspace, size_t ws_bytes,
+                      int32_t host_max_len, int32_t n_split, void* stream, size_t* ws_need = nullptr);
+
 int32_t launch_decode_latent(int mode, int phases, const lrkv_latent_cache* c, const float* q,
                              const half_t* bk, const int32_t* q_pos, float sm_scale, float* out,
                              void* ws, const LatentWorkspace& w, hipStream_t st);

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.status_string(code) and L.status_string(code) != "unknown status"
     assert lib.lrkv_version() >= 100
 
@@ -94,6 +94,30 @@ def test_decode_validation(lib):
     # workspace grows with the split count and covers every chunk
     assert lib.lrkv_decode_workspace_bytes(0, ctypes.byref(d), 4096, 128) > \
         lib.lrkv_decode_workspace_bytes(0, ctypes.byref(d), 4096, 1)
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode rejects, before any device access, a call whose
+    workspace would exceed its static scratch, and reports invalid arguments as
+    lrkv_decode_attn does."""
+    ok = ctypes.c_void_p(FAKE)
+    call = lambda mode, desc, T, ns=0, bk=ok, q=ok: lib.lrkv_decode_attn_noalloc(
+        mode, ctypes.byref(desc), q, bk, None, 0.0, ok, T, ns, None)
+    big = _latent(batch=4, capacity=32768)
+    need = lib.lrkv_decode_workspace_bytes(0, ctypes.byref(big), 32768, 1024)
+    assert need > L.NOALLOC_SCRATCH_BYTES
+    assert call(0, big, 32768, 1024) == L.LRKV_ERR_SCRATCH
+    absorbed = _latent(batch=64, capacity=65536)
+    assert lib.lrkv_decode_workspace_bytes(1, ctypes.byref(absorbed), 65536, 64) > L.NOALLOC_SCRATCH_BYTES
+    assert call(1, absorbed, 65536, 64, bk=None) == L.LRKV_ERR_SCRATCH
+    d = _latent()
+    assert call(0, d, 0) == L.LRKV_ERR_INVALID_ARG
+    assert call(0, d, 4097) == L.LRKV_ERR_INVALID_ARG
+    assert call(0, d, 4096, bk=None) == L.LRKV_ERR_INVALID_ARG
+    assert call(0, d, 4096, q=None) == L.LRKV_ERR_INVALID_ARG
+    assert call(0, _latent(rank=96), 4096) == L.LRKV_ERR_UNSUPPORTED
+    assert call(2, _paged(page_size=16), 100, bk=None) == L.LRKV_ERR_UNSUPPORTED
+    assert lib.lrkv_decode_attn_noalloc(0, None, ok, ok, None, 0.0, ok, 100, 0, None) == L.LRKV_ERR_INVALID_ARG
 
 
 def test_paged_validation(lib):
