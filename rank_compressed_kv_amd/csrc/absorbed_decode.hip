@@ -111,17 +111,17 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
     const int trow = 8 * (hn >> 2) + (hn & 3);
 
     const int n_tiles = (t_end - t_begin + 31) / 32;
-    for (int it = w; it < n_tiles; it += 4) {
-        const int t0 = t_begin + 32 * it;
-        const bool tail = t0 + 32 > t_end;
-        const long blk_base = bu * (p.cap / kTile) + t0 / kTile;
-        // every load of the tile is issued before the first MFMA: key rows
-        // (clamped to the last valid token; their scores are masked), value dims
-        // 16 v + hn at tokens 8 g .. 8 g + 7
-        half8 ka[2][KS], va[VM];
-        uint32_t kw[2][KS], vc[VM];
-        uint32_t ksc[2][KS];
-        half8 vs[NG];
+    // Tile data in registers, single-buffered but software-pipelined: the next
+    // tile's key loads are issued as soon as this tile's score MFMAs have read
+    // the key registers, its value loads once the value MFMAs have read theirs,
+    // so each load's round trip overlaps the rest of the tile before it.
+    half8 ka[2][KS], va[VM];
+    uint32_t kw[2][KS], vc[VM];
+    uint32_t ksc[2][KS];
+    half8 vs[NG];
+    // key rows (clamped to the last valid token; their scores are masked)
+    auto load_keys = [&](int tile) __attribute__((always_inline)) {
+        const int t0 = t_begin + 32 * tile;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const long row = bu * p.cap + min(t0 + trow + 4 * mt, t_end - 1);
@@ -152,6 +152,10 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
                 }
             }
         }
+    };
+    // value dims 16 v + hn at tokens 8 g .. 8 g + 7 (and int4 value scales)
+    auto load_values = [&](int tile) __attribute__((always_inline)) {
+        const long blk_base = bu * (p.cap / kTile) + (t_begin + 32 * tile) / kTile;
 #pragma unroll
         for (int v = 0; v < VM; ++v) {
             const int dim = 16 * v + hn;
@@ -164,6 +168,22 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
 #pragma unroll
             for (int gr = 0; gr < NG; ++gr)
                 vs[gr] = *reinterpret_cast<const half8*>(p.sv + (blk_base * NG + gr) * kTile + 8 * g);
+        }
+    };
+    // fp16 tiles at rank 256 fill the registers already: loaded at the top of
+    // their own iteration instead
+    constexpr bool PIPE = INT4 || R < 256;
+    if (PIPE && w < n_tiles) {
+        load_keys(w);
+        load_values(w);
+    }
+    for (int it = w; it < n_tiles; it += 4) {
+        const int t0 = t_begin + 32 * it;
+        const bool tail = t0 + 32 > t_end;
+        const bool next = PIPE && it + 4 < n_tiles;
+        if (!PIPE) {
+            load_keys(it);
+            load_values(it);
         }
         // scores: lane holds head hn at tokens 8 g + 4 mt + e
         floatx4 sc[2];
@@ -178,6 +198,7 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
                 sc[mt] = mfma16(a, qf[kk], sc[mt]);
             }
         }
+        if (next) load_keys(it + 4);
         float s8[8];
         float mt_loc = -INFINITY;
 #pragma unroll
@@ -222,6 +243,7 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
             }
 #pragma unroll
             for (int v = 0; v < VM; ++v) acc[v] = mfma16(va[v], pf, acc[v]);
+            if (next) load_values(it + 4);
         } else {
             // p in the code order (tokens 0, 4, 1, 5, 2, 6, 3, 7 of the group) times the
             // token's value scale of each 32-dim group; past t_end both are zeroed
@@ -250,6 +272,7 @@ __global__ __launch_bounds__(256, 2) void absorbed_decode(const AbsorbArgs p) {
 #pragma unroll
                 for (int v = 2 * gr; v < 2 * gr + 2; ++v) acc[v] = mfma16(value_codes(vc[v], magic), pf, acc[v]);
             }
+            if (next) load_values(it + 4);
         }
     }
 
