@@ -6,7 +6,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblrkv.so")
+# LRKV_LIBRARY selects another build of the same library (e.g. the host-checked
+# one); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("LRKV_LIBRARY") or os.path.join(_HERE, "liblrkv.so")
 
 LRKV_OK = 0
 LRKV_ERR_INVALID_ARG = -1
