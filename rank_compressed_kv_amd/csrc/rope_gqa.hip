@@ -193,8 +193,12 @@ struct GqaTile<R, true> {
             }
         }
         const uint16_t* ksp = reinterpret_cast<const uint16_t*>(kslot + KB) + c * NG + (R / 4) * g / 32;
-        ks0 = c < valid ? ksp[0] : 0u;
-        ks1 = 16 + c < valid ? ksp[16 * NG] : 0u;
+        // read unconditionally (the slot is always in the ring), then select: a
+        // conditional LDS read compiles to a branch around a wait, which splits
+        // the tile's instruction schedule
+        const uint32_t r0 = ksp[0], r1 = ksp[16 * NG];
+        ks0 = c < valid ? r0 : 0u;
+        ks1 = 16 + c < valid ? r1 : 0u;
     }
     __device__ __forceinline__ half8 key_operand(int nb, int k, uint32_t magic) const {
         return dequant_keys(kc[nb][k], nb ? ks1 : ks0, magic);
