@@ -16,7 +16,7 @@
 // block w (rows 32 w .. 32 w + 31), head h and K step ks, one contiguous 1 KB
 // block whose 16 bytes at 16 l are the A fragment of lane l (row 32 w + l%32,
 // columns 16 ks + 8 (l/32) .. + 7).
-#include "common.h"
+#include "tiles.h"
 
 #include <math.h>
 
@@ -57,10 +57,23 @@ __device__ __forceinline__ size_t qp_index(bool frag, int bu, int NH, int h, int
 // bytes) per row. Scaling by 2^e is exact, so the written value is the fp16
 // rounding of the scaled fused multiply-add.
 constexpr int kPrepLds = 32768;      // staged B^k bytes: R * s * 2 sides * 16 B (r * s <= 1024)
+constexpr int kPrepPad = kPrepLds / 8;   // one 16-byte pad after every 8 staged rows
+
+// The power of two 2^e that brings a frequency's largest |Q'| m into [2^14, 2^15)
+// (0 for an all-zero or non-finite m), clamped so that 2^e and 2^-e are normal
+// fp32 numbers.
+__device__ __forceinline__ int prep_exp(float m) {
+    const int e = (m > 0.0f && isfinite(m)) ? 14 - ilogbf(m) : 0;
+    return min(max(e, -126), 126);
+}
+
+// Staged row `x` = (KV head, side) * R + rank: 16 bytes, plus a 16-byte pad after
+// every 8 rows, so that lanes 8 ranks apart read different LDS banks.
+__device__ __forceinline__ int stage_off(int x) { return x * 8 + (x >> 3) * 8; }
 
 __device__ void prep_qprime(const PrepArgs& a, int blk) {
     __shared__ unsigned smax[8];
-    __shared__ __attribute__((aligned(16))) half_t Bs[kPrepLds / 2];
+    __shared__ __attribute__((aligned(16))) half_t Bs[(kPrepLds + kPrepPad) / 2];
     // consecutive blocks go to different XCDs: (b, u) varies fastest so that the
     // frequency groups of one unit, which share B^k's 64-byte lines, meet in one L2
     const int nbu = a.B * a.U;
@@ -100,7 +113,7 @@ __device__ void prep_qprime(const PrepArgs& a, int blk) {
             const int pc = base + 256 * m;
             if (pc < pieces) {
                 const int row = pc / (2 * a.s), sub = pc % (2 * a.s);
-                *reinterpret_cast<uint4*>(Bs + ((size_t)sub * a.R + row) * 8) = v[m];
+                *reinterpret_cast<uint4*>(Bs + stage_off(sub * a.R + row)) = v[m];
             }
         }
     }
@@ -108,8 +121,8 @@ __device__ void prep_qprime(const PrepArgs& a, int blk) {
     // Q' of ranks 8 k8 + e, frequencies i + f, rows (u, w) = (2i, 2i + 1)
     float v[8][4][2];
     if (active) {
-        const half_t* s0 = Bs + ((size_t)(2 * w) * a.R + 8 * k8) * 8 + 4 * fq;
-        const half_t* s1 = s0 + (size_t)a.R * 8;
+        const half_t* s0 = Bs + stage_off(2 * w * a.R + 8 * k8) + 4 * fq;
+        const half_t* s1 = Bs + stage_off((2 * w + 1) * a.R + 8 * k8) + 4 * fq;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const half4 b0 = *reinterpret_cast<const half4*>(s0 + 8 * e);
@@ -127,26 +140,28 @@ __device__ void prep_qprime(const PrepArgs& a, int blk) {
             float m = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) m = fmaxf(m, fmaxf(fabsf(v[e][f][0]), fabsf(v[e][f][1])));
-            for (int o = 1; o < R8 && o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+            if (R8 == 32) {
+                m = half_max32(m);                 // the half-wave holds one (head, fq)
+            } else {
+                for (int o = 1; o < R8 && o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+            }
             if ((k8 & 31) == 0) atomicMax(&smax[4 * fq + f], __float_as_uint(m));
         }
     }
     __syncthreads();
     if (t < 8) {
-        const float m = __uint_as_float(smax[t]);
-        const int e = (m > 0.0f && isfinite(m)) ? 14 - ilogbf(m) : 0;
+        const int e = prep_exp(__uint_as_float(smax[t]));
         a.qs[((size_t)b * a.U + u) * half + i0 + t] = ldexpf(1.0f, -e);
     }
     if (!active) return;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-        const float m = __uint_as_float(smax[4 * fq + f]);
-        const int ex = (m > 0.0f && isfinite(m)) ? 14 - ilogbf(m) : 0;
+        const float sc = ldexpf(1.0f, prep_exp(__uint_as_float(smax[4 * fq + f])));   // exact
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
             half8 o;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = (half_t)ldexpf(v[e][f][r2], ex);
+            for (int e = 0; e < 8; ++e) o[e] = (half_t)(v[e][f][r2] * sc);
             *reinterpret_cast<half8*>(a.qp + qp_index(frag, bu, NH, h, a.DH, a.R, 2 * (i + f) + r2, 8 * k8)) = o;
         }
     }
