@@ -26,7 +26,9 @@
 //
 // Factored pages stream through three register buffers (two pages in flight
 // while one is computed); dense pages (sink and window, a handful per
-// sequence) are handled after them without pipelining.
+// sequence) follow them through two buffers (the next one's loads issued
+// before the current one is computed) in the registers the factored pages
+// have freed.
 #include "tiles.h"
 
 #include <math.h>
@@ -448,16 +450,14 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
     }
 
     // ---- dense pages: K [P][d], V^T [d][P] in their slots
-    while (dmask) {
-        const int bit = __builtin_ctzll(dmask);
-        dmask &= dmask - 1;
-        const int slot = -1 - __builtin_amdgcn_readlane(entry, bit);
-        const int ntok = min(P, len - (p_begin + bit) * P);
+    struct DPage {
+        half8 kf[2][4];
+        half4 vf[8][2];
+    };
+    auto load_dense = [&](DPage& d, int slot) __attribute__((always_inline)) {
         const long sb = (long)bh * nd + slot;
         const rsrc_t rs_k = make_rs(a.dk + sb * P * D, P * D * 2);
         const rsrc_t rs_v = make_rs(a.dv + sb * P * D, P * D * 2);
-        half8 kf[2][4];
-        half4 vf[8][2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -466,9 +466,9 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
                     // the queries' dim order: K step s, group g, element j = dim 32 g + 8 s + code_pos_inv(j)
                     const half8 raw = ld8(rs_k, ((16 * tb + c) * D + 32 * g + 8 * s) * 2);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) kf[tb][s][j] = raw[code_pos_inv(j)];
+                    for (int j = 0; j < 8; ++j) d.kf[tb][s][j] = raw[code_pos_inv(j)];
                 } else {
-                    kf[tb][s] = ld8(rs_k, ((16 * tb + c) * D + 32 * s + 8 * g) * 2);
+                    d.kf[tb][s] = ld8(rs_k, ((16 * tb + c) * D + 32 * s + 8 * g) * 2);
                 }
             }
 #pragma unroll
@@ -477,16 +477,18 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
             for (int tb = 0; tb < 2; ++tb) {
                 // A row c of dim block mb: dim 16 mb + c, or 8 c + mb with int4 factors
                 const int dim = I4 ? 8 * c + mb : 16 * mb + c;
-                vf[mb][tb] = ld4(rs_v, (dim * P + 16 * tb + 4 * g) * 2);
+                d.vf[mb][tb] = ld4(rs_v, (dim * P + 16 * tb + 4 * g) * 2);
             }
+    };
+    auto dense = [&](DPage& d, int ntok) __attribute__((always_inline)) {
         floatx4 S[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             S[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                S[tb] = mfma16(kf[tb][s], qh[s], S[tb]);
-                S[tb] = mfma16(kf[tb][s], ql[s], S[tb]);
+                S[tb] = mfma16(d.kf[tb][s], qh[s], S[tb]);
+                S[tb] = mfma16(d.kf[tb][s], ql[s], S[tb]);
             }
         }
         half4 pb[2];
@@ -499,12 +501,34 @@ __global__ __launch_bounds__(256, NK + NV == 2 ? 2 : 1) void hybrid_decode(const
                 for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (16 * tb + 4 * g + i >= ntok) vf[mb][tb][i] = (half_t)0.0f;
+                        if (16 * tb + 4 * g + i >= ntok) d.vf[mb][tb][i] = (half_t)0.0f;
         }
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) o[mb] = mfma16k16(vf[mb][tb], pb[tb], o[mb]);
+            for (int tb = 0; tb < 2; ++tb) o[mb] = mfma16k16(d.vf[mb][tb], pb[tb], o[mb]);
+    };
+
+    // this range's dense pages, two buffers (dmask is wave-uniform)
+    if (dmask) {
+        DPage d0, d1;
+        int b0 = 0, b1 = 0;
+        auto take = [&](int& bit) __attribute__((always_inline)) -> int {
+            bit = __builtin_ctzll(dmask);
+            dmask &= dmask - 1;
+            return -1 - __builtin_amdgcn_readlane(entry, bit);
+        };
+        load_dense(d0, take(b0));
+        while (true) {
+            const bool h1 = dmask != 0;
+            if (h1) load_dense(d1, take(b1));
+            dense(d0, min(P, len - (p_begin + b0) * P));
+            if (!h1) break;
+            const bool h0 = dmask != 0;
+            if (h0) load_dense(d0, take(b0));
+            dense(d1, min(P, len - (p_begin + b1) * P));
+            if (!h0) break;
+        }
     }
 
     // ---- chunk state of the G heads: (m, l, unnormalised o)
