@@ -27,7 +27,8 @@ float64 oracle timed on the host (cpu_baseline) at one thread and at all cores.
 `python bench.py --trace-summary <kernel_trace.csv> --steps K --warmup W`
 reads a rocprofv3 kernel trace of a bench run with the same K and W and prints
 the per-step statistics of the timed steps (duration of each kernel, whole step
-from the first kernel's start to the last one's end: mean, p10, p50, p90).
+from the first kernel's start to the last one's end: mean, p10, p50, p90), and the
+partials kernel's mean over the untimed pass whose events feed roofline.achieved.
 """
 from __future__ import annotations
 
@@ -492,6 +493,47 @@ def cpu_baseline() -> dict:
     return res
 
 
+# ----------------------------------------------------------------------------- power probe
+
+def power_probe(torch, lrkv, c, w, q, Bk, n_split: int, launches: int = 2000) -> dict:
+    """The partials kernel alone, `launches` back-to-back launches in one event pair
+    after 200 untimed ones and a 0.5 s pause, on one cache: as generated, with every
+    key latent zeroed, and with the queries zeroed (the same instruction stream and
+    memory traffic, less switching in the multipliers). The cache and the prepared
+    queries are restored afterwards."""
+    mode, L = lrkv.MODE_ROPE_RECON, c.max_len
+
+    def run() -> float:
+        f = lambda: lrkv.decode_partials(mode, c.desc, None, 0.0, w, L, n_split)
+        for _ in range(200):
+            f()
+        torch.cuda.synchronize()
+        time.sleep(0.5)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(launches):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return round(a.elapsed_time(b) / launches * 1e3, 2)
+
+    prep = lambda qq: lrkv.decode_prepare(mode, c.desc, qq, Bk, None, 0.0, w, L, n_split)
+    res = {"launches": launches}
+    prep(q)
+    res["us_random"] = run()
+    hk = c.hk.clone()
+    c.hk.zero_()
+    res["us_keys_zero"] = run()
+    c.hk.copy_(hk)
+    del hk
+    prep(torch.zeros_like(q))
+    res["us_queries_zero"] = run()
+    prep(q)
+    res["us_random_again"] = run()
+    torch.cuda.synchronize()
+    return res
+
+
 # ----------------------------------------------------------------------------- kernel-trace summary
 
 def trace_summary(path: str, warmup: int, steps: int) -> dict:
@@ -528,8 +570,16 @@ def trace_summary(path: str, warmup: int, steps: int) -> dict:
     period = np.diff([s[0][1] for s in timed] + [timed[-1][3][2]]) / 1e3
     out["step_us"] = {"mean": round(float(whole.mean()), 2), "p10_p50_p90": _pct(whole)}
     out["step_period_us"] = {"mean": round(float(period.mean()), 2), "p10_p50_p90": _pct(period)}
+    # the untimed pass right after the timed steps, whose partials durations feed
+    # roofline.achieved (the same D as in main())
+    D = max(20, min(steps, 200))
+    diag = found[warmup + steps:warmup + steps + D]
+    if len(diag) == D:
+        d = np.array([(s[2][2] - s[2][1]) / 1e3 for s in diag])
+        out["partials_us_roofline_pass"] = {"launches": D, "mean": round(float(d.mean()), 2),
+                                            "p10_p50_p90": _pct(d)}
     d = np.array([(s[2][2] - s[2][1]) / 1e3 for s in found])
-    out["partials_us_all_launches_mean"] = round(float(d.mean()), 2)
+    out["partials_us_all_step_launches_mean"] = round(float(d.mean()), 2)
     return out
 
 
@@ -546,6 +596,10 @@ def main() -> int:
     ap.add_argument("--sustained", type=int, default=2000,
                     help="steps of the untimed sustained pass reported under detail (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power-probe", action="store_true",
+                    help="also time the partials kernel sustained on the benchmark cache, with its "
+                         "keys zeroed, and with the queries zeroed (how much the kernel's speed "
+                         "depends on the data it multiplies; detail.power_probe)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the timing of the other hot-path rows (absorbed, int4, hybrid, factorisation)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -732,6 +786,9 @@ def main() -> int:
             "output_finite": ok,
         },
     }
+    if args.power_probe:
+        log("bench: power probe (partials sustained on random / zeroed operands)")
+        result["detail"]["power_probe"] = power_probe(torch, lrkv, reps[0], ws[0], q, Bk, args.n_split)
     del reps, ws
     torch.cuda.empty_cache()
     log("bench: streaming-read reference")

@@ -82,7 +82,9 @@ def _write_cache_directly(cache, dk, dv, Lk, Rk, Lv, Rv, T):
 
 @pytest.mark.parametrize("B,H,G,T,rk,rv", [(2, 2, 4, 32 * 20 + 7, 12, 12), (1, 3, 4, 32 * 9, 12, 12),
                                             (2, 2, 2, 100, 12, 12), (1, 2, 8, 32 * 70 + 5, 12, 12),
-                                            (1, 2, 16, 32 * 11 + 31, 16, 32), (2, 1, 4, 32 * 13, 20, 8)])
+                                            (1, 2, 16, 32 * 11 + 31, 16, 32), (2, 1, 4, 32 * 13, 20, 8),
+                                            (1, 2, 4, 32 * 21 + 3, 4, 4), (2, 1, 4, 32 * 17 + 9, 8, 8),
+                                            (1, 2, 4, 32 * 15 + 1, 16, 16), (1, 2, 4, 32 * 12 + 5, 12, 8)])
 def test_hybrid_decode_parity(B, H, G, T, rk, rv):
     R = _R()
     say(f"hybrid decode parity: B={B} H={H} G={G} T={T} rk={rk} rv={rv}")
