@@ -5,12 +5,16 @@ Default workload: one Llama-2-7B-shaped attention layer on the RoPE path
 (d = 4096, 32 heads of 128, G-LRD groups of 4 heads -> 8 units, rank 256 per
 unit = 50% of the K/V width, fp16 latents), batch 1, T = 65536 cached tokens.
 
-One step = the whole decode hot path for one new token:
-  append the token's K/V latents (fp32 -> fp16 cache)            lrkv_append_latent
-  query preparation (rotated-basis queries)                      lrkv_decode_prepare
+One step = the whole decode hot path for one new token, one lrkv_decode_step
+call (three launches):
+  query preparation (rotated-basis queries, RoPE angle tables)
+    with the append of the token's K/V latents (fp32 -> fp16)     rope_prepare
   latent stream + on-chip reconstruction + RoPE + online
-  softmax + p.H^v, per sequence chunk                            lrkv_decode_partials
-  split-K merge                                                  lrkv_merge_partials
+  softmax + p.H^v, per sequence chunk                             rope_decode_fw
+  split-K merge, and the lengths advance                          merge_splits
+The untimed passes that bracket kernels with events issue the same work as the
+four calls lrkv_append_latent, lrkv_decode_prepare, lrkv_decode_partials and
+lrkv_merge_partials.
 Inputs are resident in HBM before the timed region. Two cache replicas are
 used in turn so that consecutive steps do not re-read the same 537 MB from the
 256 MB last-level cache. The timed region holds the K steps and nothing else
@@ -54,8 +58,10 @@ B, U, S, GQ, DH, R, THETA, TAU = 1, 8, 4, 1, 128, 256, 1e4, 96.0
 BYTES_PER_UNIT_TOKEN = 2 * R * 2                      # K and V latents, fp16
 FLOP_PER_UNIT_TOKEN = 2 * R * S * DH + 2 * S * DH + 2 * S * R
 
-# kernels of one decode step, in launch order (names as the kernel trace shows them)
-STEP_KERNELS = ("append_fp16_small", "rope_prepare", "rope_decode_fw", "merge_splits")
+# kernels of one decode step, in launch order (names as the kernel trace shows them):
+# lrkv_decode_step, and the same step issued as four calls
+STEP_KERNELS = ("rope_prepare", "rope_decode_fw", "merge_splits")
+SPLIT_STEP_KERNELS = ("append_fp16_small", "rope_prepare", "rope_decode_fw", "merge_splits")
 
 
 def log(msg: str) -> None:
@@ -538,48 +544,49 @@ def power_probe(torch, lrkv, c, w, q, Bk, n_split: int, launches: int = 2000) ->
 
 def trace_summary(path: str, warmup: int, steps: int) -> dict:
     """Per-step statistics of the timed steps from a rocprofv3 kernel trace (CSV) of
-    a bench run with the same warmup and steps: every occurrence of the step's four
-    kernels in launch order is one step; the main workload's steps come first, so
-    steps [warmup, warmup + steps) are the timed ones."""
+    a bench run with the same warmup and steps. The main workload's steps come
+    first: warmup + steps lrkv_decode_step steps (STEP_KERNELS in launch order),
+    then the untimed pass of D steps issued as four calls (SPLIT_STEP_KERNELS),
+    whose partials launches feed roofline.achieved."""
     import csv
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = set(SPLIT_STEP_KERNELS)
 
     def short(n):
-        for k in STEP_KERNELS:
+        for k in names:
             if k in n:
                 return k
         return None
     seq = [(short(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
-    found = []
+    fused, split = [], []
     i = 0
-    while i + 3 < len(seq):
-        if tuple(s[0] for s in seq[i:i + 4]) == STEP_KERNELS:
-            found.append(seq[i:i + 4])
+    while i + 2 < len(seq):
+        if i + 3 < len(seq) and tuple(x[0] for x in seq[i:i + 4]) == SPLIT_STEP_KERNELS:
+            split.append(seq[i:i + 4])
             i += 4
+        elif tuple(x[0] for x in seq[i:i + 3]) == STEP_KERNELS and not split:
+            fused.append(seq[i:i + 3])
+            i += 3
         else:
             i += 1
-    timed = found[warmup:warmup + steps]
+    timed = fused[warmup:warmup + steps]
     if len(timed) < steps:
-        raise SystemExit(f"trace holds {len(found)} steps, fewer than warmup + steps = {warmup + steps}")
-    out = {"steps_in_trace": len(found), "timed_steps": len(timed)}
+        raise SystemExit(f"trace holds {len(fused)} decode steps, fewer than warmup + steps = {warmup + steps}")
+    out = {"steps_in_trace": len(fused), "timed_steps": len(timed)}
     for j, k in enumerate(STEP_KERNELS):
-        d = np.array([(s[j][2] - s[j][1]) / 1e3 for s in timed])
+        d = np.array([(x[j][2] - x[j][1]) / 1e3 for x in timed])
         out[k + "_us"] = {"mean": round(float(d.mean()), 2), "p10_p50_p90": _pct(d)}
-    whole = np.array([(s[3][2] - s[0][1]) / 1e3 for s in timed])
-    period = np.diff([s[0][1] for s in timed] + [timed[-1][3][2]]) / 1e3
+    whole = np.array([(x[-1][2] - x[0][1]) / 1e3 for x in timed])
+    period = np.diff([x[0][1] for x in timed] + [timed[-1][-1][2]]) / 1e3
     out["step_us"] = {"mean": round(float(whole.mean()), 2), "p10_p50_p90": _pct(whole)}
     out["step_period_us"] = {"mean": round(float(period.mean()), 2), "p10_p50_p90": _pct(period)}
-    # the untimed pass right after the timed steps, whose partials durations feed
-    # roofline.achieved (the same D as in main())
+    # the untimed pass right after the timed steps (the same D as in main())
     D = max(20, min(steps, 200))
-    diag = found[warmup + steps:warmup + steps + D]
-    if len(diag) == D:
-        d = np.array([(s[2][2] - s[2][1]) / 1e3 for s in diag])
+    if len(split) >= D:
+        d = np.array([(x[2][2] - x[2][1]) / 1e3 for x in split[:D]])
         out["partials_us_roofline_pass"] = {"launches": D, "mean": round(float(d.mean()), 2),
                                             "p10_p50_p90": _pct(d)}
-    d = np.array([(s[2][2] - s[2][1]) / 1e3 for s in found])
-    out["partials_us_all_step_launches_mean"] = round(float(d.mean()), 2)
     return out
 
 
@@ -671,10 +678,17 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(i: int, ev=None) -> int:
-        """One decode step on replica i % NR; ev = two events recorded around its
-        partials kernel, or five around every phase."""
+        """One decode step on replica i % NR: one lrkv_decode_step call, or with ev the
+        same work as four calls with two events recorded around its partials kernel,
+        or five around every phase."""
         c, w = reps[i % NR], ws[i % NR]
-        five = ev is not None and len(ev) == 5
+        if ev is None:
+            L0 = c.max_len
+            lrkv.decode_step(mode, c.desc, new_k[i % 64], new_v[i % 64], 1, q, Bk, None, 0.0, out, w, L0,
+                             args.n_split, stream=stream)
+            c.host_lens += 1
+            return L0 + 1
+        five = len(ev) == 5
         if five:
             ev[0].record()
         c.append(new_k[i % 64], new_v[i % 64], stream=stream)

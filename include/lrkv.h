@@ -244,6 +244,31 @@ int32_t lrkv_decode_attn(int32_t mode, const void *cache, const float *q, const 
                          size_t ws_bytes, int32_t host_max_len, int32_t n_split, void *stream);
 
 /*
+ * One decode step: lrkv_append_latent(mode, cache, new_k, new_v, n_new,
+ * host_max_len) followed by lrkv_decode_attn(mode, cache, q, bk, q_pos,
+ * sm_scale, out, workspace, ws_bytes, host_max_len + n_new, n_split), with the
+ * same results, bit for bit, and the same cache contents and lens afterwards.
+ * host_max_len bounds the lengths before the append; the workspace is sized as
+ * lrkv_decode_workspace_bytes(mode, cache, host_max_len + n_new, n_split);
+ * q_pos NULL is each sequence's newest token after the append.
+ *
+ * Defined by: the two calls it combines (Palu digest, Method details: new
+ * tokens enter the cache as latents, then the query attends over all of them).
+ *
+ * With the RoPE mode, fp16 latents and at most 1024 new 8-element rows
+ * (batch * units * n_new * rank / 8) the append runs inside the query
+ * preparation's launch and lens advances in the merge's: three launches instead
+ * of four. Other modes and formats enqueue the append and the decode in turn.
+ *
+ * Errors: those of the two calls; every check of both is made before anything
+ * is enqueued, so a rejected call leaves the cache, lens and out unchanged.
+ */
+int32_t lrkv_decode_step(int32_t mode, const void *cache, const void *new_k, const void *new_v,
+                         int32_t n_new, const float *q, const void *bk, const int32_t *q_pos,
+                         float sm_scale, float *out, void *workspace, size_t ws_bytes,
+                         int32_t host_max_len, int32_t n_split, void *stream);
+
+/*
  * lrkv_decode_attn for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
  * same validation, kernels and result as lrkv_decode_attn with the same

@@ -35,7 +35,7 @@ EXPORTS = (
     "lrkv_decode_attn", "lrkv_decode_prepare", "lrkv_decode_partials", "lrkv_merge_partials",
     "lrkv_factor_page", "lrkv_paged_plan", "lrkv_project_workspace_bytes", "lrkv_latent_project",
     "lrkv_output_project", "lrkv_probe_stream_read", "lrkv_prefill_workspace_bytes", "lrkv_prefill_attn",
-    "lrkv_decode_attn_noalloc",
+    "lrkv_decode_attn_noalloc", "lrkv_decode_step",
 )
 
 c_i32 = ctypes.c_int32
@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.lrkv_decode_attn.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp,
                                        ctypes.c_size_t, c_i32, c_i32, c_vp]
         L.lrkv_decode_attn.restype = c_i32
+        L.lrkv_decode_step.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, ctypes.c_float, c_vp,
+                                       c_vp, ctypes.c_size_t, c_i32, c_i32, c_vp]
+        L.lrkv_decode_step.restype = c_i32
         L.lrkv_decode_attn_noalloc.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_i32, c_i32,
                                                c_vp]
         L.lrkv_decode_attn_noalloc.restype = c_i32

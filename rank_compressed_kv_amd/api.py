@@ -17,7 +17,8 @@ from ._lib import (BLOCK, FMT_FP16, FMT_INT4_G32, MODE_ABSORBED, MODE_HYBRID_PAG
                    MODE_ROPE_RECON, PAGE_EMPTY, LatentCacheDesc, PagedCacheDesc, LrkvError)
 
 __all__ = [
-    "decode_workspace_bytes", "append_latent", "decode_attn", "decode_attn_noalloc", "decode_prepare",
+    "decode_workspace_bytes", "append_latent", "decode_attn", "decode_attn_noalloc", "decode_step",
+    "decode_prepare",
     "decode_partials",
     "merge_partials", "factor_page", "paged_plan", "project_workspace_bytes", "latent_project",
     "output_project", "probe_stream_read",
@@ -63,6 +64,15 @@ def decode_attn(mode: int, desc, q, bk, q_pos, sm_scale: float, out, workspace,
     L.check(L.lib().lrkv_decode_attn(mode, ctypes.byref(desc), _p(q), _p(bk), _p(q_pos),
                                      float(sm_scale), _p(out), _p(workspace), ws_bytes,
                                      host_max_len, n_split, _stream(stream)), "lrkv_decode_attn")
+
+
+def decode_step(mode: int, desc, new_k, new_v, n_new: int, q, bk, q_pos, sm_scale: float, out, workspace,
+                host_max_len: int, n_split: int = 0, stream=None) -> None:
+    """Append n_new tokens, then decode (lrkv_decode_step): host_max_len bounds the
+    lengths before the append, the workspace covers host_max_len + n_new."""
+    L.check(L.lib().lrkv_decode_step(mode, ctypes.byref(desc), _p(new_k), _p(new_v), n_new, _p(q), _p(bk),
+                                      _p(q_pos), float(sm_scale), _p(out), _p(workspace), _ws(workspace),
+                                      host_max_len, n_split, _stream(stream)), "lrkv_decode_step")
 
 
 def decode_attn_noalloc(mode: int, desc, q, bk, q_pos, sm_scale: float, out, host_max_len: int,
@@ -239,6 +249,33 @@ class LatentCache:
         if workspace is None:
             workspace = self.workspace(mode, n_split)
         decode_attn(mode, self.desc, q, bk, q_pos, sm_scale, out, workspace, self.max_len, n_split, stream)
+        return out
+
+    def step(self, mode: int, new_k: torch.Tensor, new_v: torch.Tensor, q: torch.Tensor,
+             bk: torch.Tensor | None = None, q_pos: torch.Tensor | None = None, sm_scale: float = 0.0,
+             n_split: int = 0, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+        """append(new_k, new_v) then decode(mode, q, ...) in one call (lrkv_decode_step);
+        the workspace must cover the lengths after the append."""
+        n_new = new_k.shape[2]
+        _need(new_k, torch.float32, (self.B, self.U, n_new, self.r), "new_k")
+        _need(new_v, torch.float32, (self.B, self.U, n_new, self.r), "new_v")
+        qdim = self.dh if mode == MODE_ROPE_RECON else self.r
+        _need(q, torch.float32, (self.B, self.Hq, qdim), "q")
+        if bk is not None:
+            _need(bk, torch.float16, (self.U, self.r, self.s * self.dh), "bk")
+        if q_pos is not None:
+            _need(q_pos, torch.int32, (self.B,), "q_pos")
+        if out is None:
+            out = torch.empty((self.B, self.Hq, self.r), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            n = decode_workspace_bytes(mode, self.desc, self.max_len + n_new, n_split)
+            if n == 0:
+                raise LrkvError(L.LRKV_ERR_INVALID_ARG, "lrkv_decode_workspace_bytes")
+            workspace = torch.empty(n, dtype=torch.uint8, device=self.hk.device)
+        decode_step(mode, self.desc, new_k, new_v, n_new, q, bk, q_pos, sm_scale, out, workspace, self.max_len,
+                    n_split, stream)
+        self.host_lens += n_new
         return out
 
     def prefill_workspace(self, m_tokens: int) -> torch.Tensor:

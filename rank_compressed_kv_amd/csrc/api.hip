@@ -148,6 +148,26 @@ static int32_t check_paged(const lrkv_paged_cache* c) {
 
 using namespace lrkv;
 
+// Every check lrkv_append_latent makes before it enqueues anything.
+static int32_t check_append(int32_t mode, const void* cache, const void* new_k, const void* new_v,
+                            int32_t n_new, int32_t host_max_len) {
+    if (!cache || !new_k || !new_v || n_new < 1 || host_max_len < 0) return LRKV_ERR_INVALID_ARG;
+    if (!aligned16(new_k) || !aligned16(new_v)) return LRKV_ERR_INVALID_ARG;
+    if (mode == LRKV_MODE_HYBRID_PAGED) {
+        const lrkv_paged_cache* c = (const lrkv_paged_cache*)cache;
+        int32_t rc = check_paged(c);
+        if (rc != LRKV_OK) return rc;
+        if ((long)host_max_len + n_new > (long)c->max_pages * c->page_size) return LRKV_ERR_CAPACITY;
+        return LRKV_OK;
+    }
+    if (mode != LRKV_MODE_ROPE_RECON && mode != LRKV_MODE_ABSORBED) return LRKV_ERR_INVALID_ARG;
+    const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
+    int32_t rc = check_latent(c);
+    if (rc != LRKV_OK) return rc;
+    if ((long)host_max_len + n_new > c->capacity) return LRKV_ERR_CAPACITY;
+    return LRKV_OK;
+}
+
 extern "C" {
 
 const char* lrkv_status_string(int32_t s) {
@@ -183,22 +203,14 @@ size_t lrkv_decode_workspace_bytes(int32_t mode, const void* cache, int32_t host
 
 int32_t lrkv_append_latent(int32_t mode, const void* cache, const void* new_k, const void* new_v,
                            int32_t n_new, int32_t host_max_len, void* stream) {
-    if (!cache || !new_k || !new_v || n_new < 1 || host_max_len < 0) return LRKV_ERR_INVALID_ARG;
-    if (!aligned16(new_k) || !aligned16(new_v)) return LRKV_ERR_INVALID_ARG;
-    hipStream_t st = (hipStream_t)stream;
-    if (mode == LRKV_MODE_HYBRID_PAGED) {
-        const lrkv_paged_cache* c = (const lrkv_paged_cache*)cache;
-        int32_t rc = check_paged(c);
-        if (rc != LRKV_OK) return rc;
-        if ((long)host_max_len + n_new > (long)c->max_pages * c->page_size) return LRKV_ERR_CAPACITY;
-        return launch_append_paged(c, (const half_t*)new_k, (const half_t*)new_v, n_new, st);
-    }
-    if (mode != LRKV_MODE_ROPE_RECON && mode != LRKV_MODE_ABSORBED) return LRKV_ERR_INVALID_ARG;
-    const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
-    int32_t rc = check_latent(c);
+    const int32_t rc = check_append(mode, cache, new_k, new_v, n_new, host_max_len);
     if (rc != LRKV_OK) return rc;
-    if ((long)host_max_len + n_new > c->capacity) return LRKV_ERR_CAPACITY;
-    return launch_append_latent(c, (const float*)new_k, (const float*)new_v, n_new, st);
+    hipStream_t st = (hipStream_t)stream;
+    if (mode == LRKV_MODE_HYBRID_PAGED)
+        return launch_append_paged((const lrkv_paged_cache*)cache, (const half_t*)new_k, (const half_t*)new_v,
+                                   n_new, st);
+    return launch_append_latent((const lrkv_latent_cache*)cache, (const float*)new_k, (const float*)new_v,
+                                n_new, st);
 }
 
 }  // extern "C"
@@ -210,7 +222,7 @@ int32_t lrkv_append_latent(int32_t mode, const void* cache, const void* new_k, c
 int32_t lrkv::decode_common(int32_t mode, int phases, const void* cache, const float* q,
                              const void* bk, const int32_t* q_pos, float sm_scale, float* out,
                              void* workspace, size_t ws_bytes, int32_t host_max_len, int32_t n_split,
-                             void* stream, size_t* ws_need) {
+                             void* stream, size_t* ws_need, const FusedAppend* app) {
     if (!cache || host_max_len < 1) return LRKV_ERR_INVALID_ARG;
     if ((phases & kPhaseMerge) && !out) return LRKV_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
@@ -252,7 +264,7 @@ int32_t lrkv::decode_common(int32_t mode, int phases, const void* cache, const f
     if (!workspace || ws_bytes < w.total || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c->head_dim);
     return launch_decode_latent(mode, phases, c, q, (const half_t*)bk, q_pos, scale, out, workspace,
-                                w, st);
+                                w, st, app);
 }
 
 extern "C" {
@@ -263,6 +275,34 @@ int32_t lrkv_decode_attn(int32_t mode, const void* cache, const float* q, const 
     if (!q) return LRKV_ERR_INVALID_ARG;
     return decode_common(mode, kPhaseAll, cache, q, bk, q_pos, sm_scale, out, workspace, ws_bytes,
                          host_max_len, n_split, stream);
+}
+
+int32_t lrkv_decode_step(int32_t mode, const void* cache, const void* new_k, const void* new_v,
+                         int32_t n_new, const float* q, const void* bk, const int32_t* q_pos,
+                         float sm_scale, float* out, void* workspace, size_t ws_bytes,
+                         int32_t host_max_len, int32_t n_split, void* stream) {
+    // both halves validated before anything is enqueued
+    int32_t rc = check_append(mode, cache, new_k, new_v, n_new, host_max_len);
+    if (rc != LRKV_OK) return rc;
+    if (!q) return LRKV_ERR_INVALID_ARG;
+    const int32_t len_after = host_max_len + n_new;
+    size_t need = 0;
+    rc = decode_common(mode, kPhaseAll, cache, q, bk, q_pos, sm_scale, out, workspace, ws_bytes, len_after,
+                       n_split, stream, &need);
+    if (rc != LRKV_OK) return rc;
+    if (!workspace || ws_bytes < need || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
+    if (mode == LRKV_MODE_ROPE_RECON) {
+        const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
+        if (c->fmt == LRKV_FMT_FP16 && (long)c->batch * c->units * n_new * (c->rank / 8) <= kSmallAppendRows) {
+            const FusedAppend app{(const float*)new_k, (const float*)new_v, n_new};
+            return decode_common(mode, kPhaseAll, cache, q, bk, q_pos, sm_scale, out, workspace, ws_bytes,
+                                 len_after, n_split, stream, nullptr, &app);
+        }
+    }
+    rc = lrkv_append_latent(mode, cache, new_k, new_v, n_new, host_max_len, stream);
+    if (rc != LRKV_OK) return rc;
+    return decode_common(mode, kPhaseAll, cache, q, bk, q_pos, sm_scale, out, workspace, ws_bytes, len_after,
+                         n_split, stream);
 }
 
 int32_t lrkv_decode_prepare(int32_t mode, const void* cache, const float* q, const void* bk,

@@ -6,7 +6,7 @@
 // go to the newest dense page. The int4 rule (Shard post, section 5, step 4:
 // symmetric [-7, 7]; Palu digest, Supplementary details: per-token groups of
 // 32) is documented in lrkv.h.
-#include "common.h"
+#include "append_dev.h"
 
 namespace lrkv {
 namespace {
@@ -58,27 +58,7 @@ __global__ __launch_bounds__(256) void append_fp16_small(const float* __restrict
                                                          half_t* __restrict__ hv,
                                                          int32_t* __restrict__ lens, int B, int U,
                                                          int r, int cap, int n_new) {
-    const int r8 = r / 8;
-    const int total = B * U * n_new * r8;
-    for (int e = threadIdx.x; e < total; e += blockDim.x) {
-        const int d8 = e % r8;
-        int rest = e / r8;
-        const int i = rest % n_new;
-        rest /= n_new;
-        const int u = rest % U;
-        const int b = rest / U;
-        const int pos = lens[b] + i;
-        if (pos >= cap) continue;
-        const long src = (((long)b * U + u) * n_new + i) * r + d8 * 8;
-        const long bu = (long)b * U + u;
-        half8 kh;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) kh[k] = (half_t)nk[src + k];
-        *reinterpret_cast<half8*>(hk + (bu * cap + pos) * r + d8 * 8) = kh;
-        half_t* vblk = hv + ((bu * (cap / kTile) + pos / kTile) * r + d8 * 8) * kTile + pos % kTile;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) vblk[k * kTile] = (half_t)nv[src + k];
-    }
+    append_fp16_rows(nk, nv, hk, hv, lens, B, U, r, cap, n_new, threadIdx.x, blockDim.x);
     __syncthreads();
     for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] += n_new;
 }
@@ -201,7 +181,7 @@ inline unsigned blocks_for(long n, int bs) { return (unsigned)((n + bs - 1) / bs
 int32_t launch_append_latent(const lrkv_latent_cache* c, const float* nk, const float* nv,
                              int n_new, hipStream_t st) {
     const int B = c->batch, U = c->units, r = c->rank, cap = c->capacity;
-    if (c->fmt == LRKV_FMT_FP16 && (long)B * U * n_new * (r / 8) <= 1024) {
+    if (c->fmt == LRKV_FMT_FP16 && (long)B * U * n_new * (r / 8) <= kSmallAppendRows) {
         hipLaunchKernelGGL(append_fp16_small, dim3(1), dim3(256), 0, st, nk, nv, (half_t*)c->hk,
                            (half_t*)c->hv, c->lens, B, U, r, cap, n_new);
         return last_launch_status();

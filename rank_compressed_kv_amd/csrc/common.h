@@ -18,6 +18,10 @@ constexpr int kWave = 64;
 constexpr int kTile = 32;          // tokens per attention tile == cache block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplit = 1024;    // sequence chunks merged per head (merge kernel's LDS)
+// A decode-size fp16 append runs in one workgroup of 256 threads (and inside the
+// query preparation of lrkv_decode_step) when it has at most this many 8-element
+// rows (B * U * n_new * r / 8).
+constexpr int kSmallAppendRows = 1024;
 constexpr int kMaxRopeTiles = 256; // tiles per RoPE chunk: bounds the angle-rotation drift
 
 // ---------------------------------------------------------------- MFMA wrappers
@@ -118,15 +122,24 @@ constexpr int kPhasePrepare = 1, kPhasePartials = 2, kPhaseMerge = 4, kPhaseAll 
 constexpr int kQpRowMajor = 0, kQpFragments = 1, kQpGqaFragments = 2;
 bool use_gqa_kernel(const LatentGeom& g);
 
+// The new tokens of lrkv_decode_step when they are appended inside the decode's
+// own launches (fp32 [B][U][n_new][R], like lrkv_append_latent's inputs).
+struct FusedAppend {
+    const float* nk;
+    const float* nv;
+    int n_new;
+};
 // Validation and dispatch shared by every decode entry point (api.hip). With
 // ws_need non-null it only validates and stores the workspace size needed.
 int32_t decode_common(int32_t mode, int phases, const void* cache, const float* q, const void* bk,
                       const int32_t* q_pos, float sm_scale, float* out, void* workspace, size_t ws_bytes,
-                      int32_t host_max_len, int32_t n_split, void* stream, size_t* ws_need = nullptr);
+                      int32_t host_max_len, int32_t n_split, void* stream, size_t* ws_need = nullptr,
+                      const FusedAppend* app = nullptr);
 
 int32_t launch_decode_latent(int mode, int phases, const lrkv_latent_cache* c, const float* q,
                              const half_t* bk, const int32_t* q_pos, float sm_scale, float* out,
-                             void* ws, const LatentWorkspace& w, hipStream_t st);
+                             void* ws, const LatentWorkspace& w, hipStream_t st,
+                             const FusedAppend* app = nullptr);
 
 struct PagedWorkspace {
     size_t part_off, total;

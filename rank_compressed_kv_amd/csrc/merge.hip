@@ -11,9 +11,14 @@ namespace {
 // out[b][j][d] = sum_c 2^(m_c - M) acc_c[d] / sum_c 2^(m_c - M) l_c over the
 // n_split chunks (at most 1024); empty chunks (m = -inf) contribute nothing.
 // One wave per (sequence, head, 64 output dims): the chunk maxima and weights
-// go through LDS, reductions are wave-wide shuffles.
+// go through LDS, reductions are wave-wide shuffles. With `lens` non-null the
+// first wave also adds `bump` to lens[0 .. B) (lrkv_decode_step: the step's
+// appended tokens, once every kernel that reads lens before them has run).
 __global__ __launch_bounds__(64) void merge_splits(const float* __restrict__ part,
-                                                   float* __restrict__ out, int n_split, int D) {
+                                                   float* __restrict__ out, int n_split, int D,
+                                                   int32_t* __restrict__ lens, int B, int bump) {
+    if (lens && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int b = threadIdx.x; b < B; b += 64) lens[b] += bump;
     constexpr int kPre = 32;                   // chunks whose outputs are requested up front
     __shared__ float wts[1024], lsum[1024];
     const long bj = blockIdx.x;
@@ -67,7 +72,14 @@ __global__ __launch_bounds__(64) void merge_splits(const float* __restrict__ par
 }  // namespace
 
 void launch_merge(const float* part, float* out, int BH, int n_split, int D, hipStream_t st) {
-    hipLaunchKernelGGL(merge_splits, dim3(BH, (D + 63) / 64), dim3(64), 0, st, part, out, n_split, D);
+    hipLaunchKernelGGL(merge_splits, dim3(BH, (D + 63) / 64), dim3(64), 0, st, part, out, n_split, D,
+                       (int32_t*)nullptr, 0, 0);
+}
+
+void launch_merge_bump(const float* part, float* out, int BH, int n_split, int D, hipStream_t st,
+                       int32_t* lens, int B, int bump) {
+    hipLaunchKernelGGL(merge_splits, dim3(BH, (D + 63) / 64), dim3(64), 0, st, part, out, n_split, D,
+                       lens, B, bump);
 }
 
 }  // namespace lrkv

@@ -33,6 +33,7 @@ struct RopeArgs {
     AngleTables ang;
     float* part;          // [B][Hq][n_split][R + 2]
     int B, U, NH, cap, n_split, chunk, n_groups;
+    int pending;          // tokens appended in this step whose lens update is still to come
 };
 
 namespace {
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void rope_decode(const RopeArgs p) {
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int Hq = p.U * p.NH, j0 = u * p.NH + hg * NHW;
-    const int len = min(p.lens[b], p.cap);
+    const int len = min(p.lens[b] + p.pending, p.cap);
     const int t_begin = split * p.chunk;
     const int t_end = min(len, t_begin + p.chunk);
     const long bu = (long)b * p.U + u;
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256, 1) void rope_decode_fw(const RopeArgs p) {
     // (load addresses, LDS bases) is scalar arithmetic
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int Hq = p.U * NH;
-    const int len = min(p.lens[b], p.cap);
+    const int len = min(p.lens[b] + p.pending, p.cap);
     const int t_begin = split * p.chunk;
     const int t_end = min(len, t_begin + p.chunk);
     const long bu = (long)b * p.U + u;
@@ -663,12 +664,12 @@ bool rope_shape_supported(int r, int dh, int nh) {
 }
 
 int32_t launch_rope_decode(const lrkv_latent_cache* c, const half_t* qp, const float* qs,
-                           const float2* angles, float* part, int n_split, int chunk, hipStream_t st) {
+                           const float2* angles, float* part, int n_split, int chunk, hipStream_t st, int pending) {
     const int nh = c->kv_per_unit * c->q_per_kv, r = c->rank, dh = c->head_dim;
     const bool int4 = c->fmt == LRKV_FMT_INT4_G32;
     RopeArgs a{c->hk, c->hv, (const half_t*)c->sk, (const half_t*)c->sv, c->lens, qp, qs,
                AngleTables{angles, angles + dh / 2, angles + 33 * (dh / 2)}, part, c->batch,
-               c->units, nh, c->capacity, n_split, chunk, 0};
+               c->units, nh, c->capacity, n_split, chunk, 0, pending};
     if (use_frequency_wave(c)) {
         a.n_groups = n_split * a.U * a.B;
         hipLaunchKernelGGL(rope_decode_fw<256>, dim3(a.n_groups), dim3(256), 0, st, a);

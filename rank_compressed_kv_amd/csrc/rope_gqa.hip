@@ -57,6 +57,7 @@ struct GqaArgs {
     AngleTables ang;
     float* part;           // [B][Hq][n_split][R + 2]
     int B, U, cap, n_split, chunk, n_waves;
+    int pending;           // tokens appended in this step whose lens update is still to come
 };
 
 namespace {
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void rope_decode_gqa(const GqaArgs p) {
     const int gw = blockIdx.x * 4 + w;
     if (gw >= p.n_waves) return;
     const int split = gw % p.n_split, bu = gw / p.n_split, u = bu % p.U, b = bu / p.U;
-    const int len = min(p.lens[b], p.cap);
+    const int len = min(p.lens[b] + p.pending, p.cap);
     const int t_begin = split * p.chunk, t_end = min(len, t_begin + p.chunk);
     const int Hq = p.U * NH, j0 = u * NH;
     float* part = p.part + ((long)(b * Hq + j0) * p.n_split + split) * (R + 2);
@@ -618,12 +619,12 @@ bool use_gqa_kernel(const LatentGeom& g) {
 // `qbuf`: what the preparation wrote, B^k fragments [U][128][r] fp16 followed by
 // the scaled queries [B][Hq][128] fp32.
 int32_t launch_rope_gqa(const lrkv_latent_cache* c, const half_t* qbuf, const float2* angles, float* part,
-                        int n_split, int chunk, hipStream_t st) {
+                        int n_split, int chunk, hipStream_t st, int pending) {
     const LatentGeom g = latent_geom(c);
     const float* q = reinterpret_cast<const float*>(qbuf + (long)g.U * 128 * g.r);
     GqaArgs a{c->hk, c->hv, (const half_t*)c->sk, (const half_t*)c->sv, c->lens, q, qbuf,
               AngleTables{angles, angles + 64, angles + 33 * 64}, part, g.B, g.U, g.cap,
-              n_split, chunk, g.B * g.U * n_split};
+              n_split, chunk, g.B * g.U * n_split, pending};
     const bool int4 = g.fmt == LRKV_FMT_INT4_G32;
     if (g.r == 64) {
         if (int4) launch_gqa<64, 4, true>(a, st);

@@ -10,12 +10,16 @@
 // This step writes Q' = [u_0, w_0, u_1, w_1, ...] (d_h rows of r values, fp16)
 // for every head, and the cos/sin tables of the phi_i (fp64 angles, fp32 values).
 // One launch; its blocks take one of three roles: Q' (or, for the grouped-query
-// kernel, B^k fragments and scaled queries), then the angle tables.
+// kernel, B^k fragments and scaled queries), then the angle tables. For
+// lrkv_decode_step a first block also appends the step's new fp16 latents
+// without touching lens: `pending` tokens then count as cached (the merge of
+// the same step adds them to lens once every reader of lens has finished).
 // Q' is stored row-major per head, or (for the rank-256, d_h-128, 4-head units
 // of the frequency-wave kernel) in MFMA-fragment order: for unit (b, u), row
 // block w (rows 32 w .. 32 w + 31), head h and K step ks, one contiguous 1 KB
 // block whose 16 bytes at 16 l are the A fragment of lane l (row 32 w + l%32,
 // columns 16 ks + 8 (l/32) .. + 7).
+#include "append_dev.h"
 #include "tiles.h"
 
 #include <math.h>
@@ -38,6 +42,11 @@ struct PrepArgs {
     float scale;
     int qmode, int4;
     int n_q, n_s;            // blocks of the Q' / B^k role and of the query-scaling role
+    // fused append (lrkv_decode_step): n_app = 1 block writes the `pending` new
+    // tokens (nk, nv [B][U][pending][R] fp32) into hk / hv
+    int n_app, pending, cap;
+    const float *nk, *nv;
+    half_t *hk, *hv;
 };
 
 __device__ __forceinline__ size_t qp_index(bool frag, int bu, int NH, int h, int DH, int R, int row, int k) {
@@ -211,7 +220,7 @@ __device__ void prep_angles(const PrepArgs& a, int blk) {
         n = row - 1;
     } else {
         const int b = (row - 33) / a.n_split, c = (row - 33) % a.n_split;
-        const long qpos = a.q_pos ? a.q_pos[b] : (long)a.lens[b] - 1;
+        const long qpos = a.q_pos ? a.q_pos[b] : (long)a.lens[b] + a.pending - 1;
         n = (long)c * a.chunk - qpos;
     }
     const double rho = a.theta > 0.0 ? exp2(-2.0 * f / (2.0 * half) * log2(a.theta)) / kTwoPi : 0.0;
@@ -223,7 +232,11 @@ __device__ void prep_angles(const PrepArgs& a, int blk) {
 }
 
 __global__ __launch_bounds__(256) void rope_prepare(const PrepArgs a) {
-    const int blk = blockIdx.x;
+    if ((int)blockIdx.x < a.n_app) {
+        append_fp16_rows(a.nk, a.nv, a.hk, a.hv, a.lens, a.B, a.U, a.R, a.cap, a.pending, threadIdx.x, 256);
+        return;
+    }
+    const int blk = blockIdx.x - a.n_app;
     if (blk < a.n_q) {
         if (a.qmode == kQpGqaFragments) prep_bfrag(a, blk);
         else prep_qprime(a, blk);
@@ -239,9 +252,10 @@ __global__ __launch_bounds__(256) void rope_prepare(const PrepArgs a) {
 void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, const int32_t* lens,
                       half_t* qp, float* qs, float2* angles, int B, int U, int s, int gq, int DH,
                       int R, int n_split, int chunk, double theta, float scale, int qmode,
-                      bool int4, hipStream_t st) {
+                      bool int4, hipStream_t st, int pending, const float* nk, const float* nv,
+                      half_t* hk, half_t* hv, int cap) {
     PrepArgs a{q, bk, q_pos, lens, qp, qs, angles, B, U, s, gq, DH, R, n_split, chunk, theta, scale,
-               qmode, int4 ? 1 : 0, 0, 0};
+               qmode, int4 ? 1 : 0, 0, 0, nk ? 1 : 0, pending, cap, nk, nv, hk, hv};
     if (qmode == kQpGqaFragments) {
         a.n_q = (int)(((long)U * 128 * R + 255) / 256);
         a.n_s = (int)(((long)B * U * s * gq * DH + 255) / 256);
@@ -249,7 +263,7 @@ void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, co
         a.n_q = B * U * (DH / 16);
     }
     const int n_ang = ((33 + B * n_split) * (DH / 2) + 255) / 256;
-    hipLaunchKernelGGL(rope_prepare, dim3(a.n_q + a.n_s + n_ang), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(rope_prepare, dim3(a.n_app + a.n_q + a.n_s + n_ang), dim3(256), 0, st, a);
 }
 
 }  // namespace lrkv

@@ -250,3 +250,31 @@ def test_prefill_validation(lib):
     assert call(i4) == L.LRKV_ERR_UNSUPPORTED
     assert call(_latent(rank=128)) == L.LRKV_ERR_UNSUPPORTED
     assert call(_latent(head_dim=64)) == L.LRKV_ERR_UNSUPPORTED
+
+
+def test_decode_step_validation(lib):
+    """lrkv_decode_step rejects before enqueueing: the append's checks (capacity,
+    pointers, alignment), then the decode's (queries, workspace for the length after
+    the append)."""
+    d = _latent(batch=1, units=8, kv_per_unit=4, rank=256, capacity=4096)
+    ok = ctypes.c_void_p(FAKE)
+    need = lib.lrkv_decode_workspace_bytes(0, ctypes.byref(d), 4001, 0)
+    assert need > 0
+    args = lambda **kw: dict(dict(mode=0, nk=ok, nv=ok, n=1, q=ok, bk=ok, out=ok, ws=ok, wsb=need, hml=4000), **kw)
+    def call(**kw):
+        a = args(**kw)
+        return lib.lrkv_decode_step(a["mode"], ctypes.byref(d), a["nk"], a["nv"], a["n"], a["q"], a["bk"], None,
+                                    0.0, a["out"], a["ws"], a["wsb"], a["hml"], 0, None)
+    assert call(hml=4096) == L.LRKV_ERR_CAPACITY
+    assert call(hml=4095, n=2) == L.LRKV_ERR_CAPACITY
+    assert call(n=0) == L.LRKV_ERR_INVALID_ARG
+    assert call(nk=None) == L.LRKV_ERR_INVALID_ARG
+    assert call(nk=ctypes.c_void_p(FAKE + 4)) == L.LRKV_ERR_INVALID_ARG
+    assert call(q=None) == L.LRKV_ERR_INVALID_ARG
+    assert call(bk=None) == L.LRKV_ERR_INVALID_ARG
+    assert call(out=None) == L.LRKV_ERR_INVALID_ARG
+    assert call(mode=7) == L.LRKV_ERR_INVALID_ARG
+    assert call(ws=None) == L.LRKV_ERR_WORKSPACE
+    assert call(wsb=need - 1) == L.LRKV_ERR_WORKSPACE
+    # absorbed mode takes no B^k
+    assert call(mode=1) == L.LRKV_ERR_INVALID_ARG
