@@ -393,6 +393,30 @@ class PagedCache:
         append_latent(MODE_HYBRID_PAGED, self.desc, k, v, 1, self.max_len, stream)
         self.host_lens += 1
 
+    def step(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, sm_scale: float = 0.0,
+             n_split: int = 0, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+             max_sweeps: int = 0, stream=None) -> torch.Tensor:
+        """append(k, v) then decode(q) (lrkv_decode_step): the page that leaves the
+        window (if any) is factored first, as append does; the workspace must cover
+        the lengths after the append."""
+        _need(k, torch.float16, (self.B, self.H, 1, self.d), "k")
+        _need(v, torch.float16, (self.B, self.H, 1, self.d), "v")
+        _need(q, torch.float32, (self.B, self.H * self.G, self.d), "q")
+        pages = self._pages(1)
+        if pages is not None:
+            factor_page(self.desc, pages, pages.shape[0], None, None, 0, max_sweeps, stream)
+        if out is None:
+            out = torch.empty((self.B, self.H * self.G, self.d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            n = decode_workspace_bytes(MODE_HYBRID_PAGED, self.desc, self.max_len + 1, n_split)
+            if n == 0:
+                raise LrkvError(L.LRKV_ERR_INVALID_ARG, "lrkv_decode_workspace_bytes")
+            workspace = torch.empty(n, dtype=torch.uint8, device=self.dense_k.device)
+        decode_step(MODE_HYBRID_PAGED, self.desc, k, v, 1, q, None, None, sm_scale, out, workspace,
+                    self.max_len, n_split, stream)
+        self.host_lens += 1
+        return out
+
     def workspace(self, n_split: int = 0) -> torch.Tensor:
         n = decode_workspace_bytes(MODE_HYBRID_PAGED, self.desc, self.max_len, n_split)
         if n == 0:

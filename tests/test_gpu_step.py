@@ -154,3 +154,37 @@ def test_rejected_step_leaves_cache_unchanged(name):
     for x, y in zip(before, _snapshot(c)):
         assert torch.equal(x, y)
     assert bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("fmt", ["fp16", "int4"])
+def test_paged_step_equals_append_then_decode(fmt):
+    """Hybrid paged cache: 40 steps across page boundaries (the page leaving the
+    window is factored first in both), outputs, factors, dense pages, page table and
+    lengths bit-identical to append + decode."""
+    R = _R()
+    B, H, G, P = 2, 2, 4, 32
+    T0 = 32 * 9 + 20
+    say(f"paged decode_step vs append+decode: {fmt}, T0={T0}, 40 steps")
+    ff = R.FMT_FP16 if fmt == "fp16" else R.FMT_INT4_G32
+    dense = synth.paged_dense(71, B, H, T0 + 40, 128)
+    k = torch.from_numpy(dense["k"]).half().cuda()
+    v = torch.from_numpy(dense["v"]).half().cuda()
+    caches = []
+    for _ in range(2):
+        c = R.PagedCache(B, H, G, 128, P, 1, 4, 12, 12, max_pages=(T0 + 40) // P + 4, factor_fmt=ff)
+        c.prefill(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous())
+        caches.append(c)
+    ca, cb = caches
+    for i in range(40):
+        t = T0 + i
+        kt, vt = k[:, :, t:t + 1].contiguous(), v[:, :, t:t + 1].contiguous()
+        q = to_dev(synth.queries(400 + i, B, H * G, 128))
+        oa = ca.step(kt, vt, q)
+        cb.append(kt, vt)
+        ob = cb.decode(q)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), i
+    for name in ("dense_k", "dense_v", "lk", "rk", "lv", "rv", "lk_s", "rk_s", "lv_s", "rv_s", "page_table",
+                 "lens"):
+        if getattr(ca, name) is not None:
+            assert torch.equal(getattr(ca, name), getattr(cb, name)), name
