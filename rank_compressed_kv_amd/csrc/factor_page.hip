@@ -12,7 +12,9 @@
 //      of 2x2 block updates (rows and columns together) plus the eigenvector
 //      columns, written to the next round's positions in a second buffer. A
 //      pair is skipped when |g_pq| <= 1e-6 trace(G); the sweeps stop when a
-//      sweep skips every pair or after max_sweeps.
+//      sweep skips every pair, when the off-diagonal Frobenius norm after a
+//      sweep is at most 1e-4 trace(G) (the rank-r subspace error is second
+//      order in it), or after max_sweeps.
 //   3. Eigenvalues sorted descending (ties: lower index first); L = the first r
 //      eigenvectors rounded to fp16, R = L^T X accumulated in fp32, stored fp16
 //      (value pages transposed: L^T and R^T, the layout the decode reads). With
@@ -194,6 +196,21 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
             cur ^= 1;
         }
         if (!__any(rotated)) break;
+        // off-diagonal Frobenius norm of G after the sweep (lane l: rows l / 2, columns
+        // of half l % 2), against 1e-4 trace(G)
+        float off = 0.0f;
+        {
+            float (*Gc)[LD] = Gb[cur];
+            const int row = l >> 1, c0 = 16 * (l & 1);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float v = Gc[row][c0 + j];
+                off = c0 + j == row ? off : fmaf(v, v, off);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o, kWave);
+        if (off <= 1e-8f * tr * tr) break;
     }
     float (*G)[LD] = Gb[cur];
     float (*V)[LD] = Vb[cur];
