@@ -5,11 +5,11 @@
 // vectors of X, so L = Q_r and R = Q_r^T X are the truncated-SVD factors
 // (R = S_r W_r^T). Pages have one shape, so many are factored in one launch.
 //
-// One single-wave workgroup per page matrix (K or V of one page):
+// One workgroup of four waves per page matrix (K or V of one page):
 //   1. X (fp16) -> G on the 32x32x16 MFMA (A and B fragments are the same rows).
 //   2. Cyclic Jacobi on G in LDS, fp32, round-robin (circle-method) ordering:
 //      each round rotates 16 disjoint index pairs at once, applied as one pass
-//      of 2x2 block updates (rows and columns together) plus the eigenvector
+//      of 2x2 block updates (one block per thread; rows and columns together) plus the eigenvector
 //      columns, written to the next round's positions in a second buffer. A
 //      pair is skipped when |g_pq| <= 1e-6 trace(G); the sweeps stop when a
 //      sweep skips every pair, when the off-diagonal Frobenius norm after a
@@ -66,12 +66,6 @@ __device__ bool resolve(const FactorArgs& a, int idx, bool is_v, int& b, int& h,
     return true;
 }
 
-__device__ __forceinline__ void wave_sync_lds() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Circle-method position map of the round-robin ordering: positions 2k and
 // 2k+1 hold the pair rotated in a round; after the round, the element at
 // position x moves to sigma(x). Position 0 stays; the other 31 positions form
@@ -86,15 +80,16 @@ __device__ __forceinline__ int sigma(int x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
+__global__ __launch_bounds__(256) void factor_pages(const FactorArgs a) {
     constexpr int P = 32, LD = P + 1;
     __shared__ float Gb[2][P][LD];     // G, double-buffered across rounds
     __shared__ float Vb[2][P][LD];     // eigenvectors (columns), likewise
     __shared__ half_t Xs[P][D + 8];
     __shared__ float rot[16][2];
     __shared__ int order[P];
+    __shared__ int stop;
 
-    const int l = threadIdx.x;
+    const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
     const int m = blockIdx.x;
     if (m >= 2 * a.n_pages) return;
     const int idx = m >> 1;
@@ -105,46 +100,49 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
     if (!resolve<D>(a, idx, is_v, b, h, pg, X, dim_major)) return;
     const int r = is_v ? a.rank_v : a.rank_k;
 
-    // ---- Gram matrix on the MFMA; X kept in LDS for R = L^T X
-    floatx16 acc = floatx16{};
+    // ---- Gram matrix on the MFMA (wave 0); X kept in LDS for R = L^T X
     if (dim_major) {
         // X^T [D][P] in global memory: transpose into Xs first
-        for (int e = l; e < D * P / 8; e += 64) {
+        for (int e = tid; e < D * P / 8; e += 256) {
             const int dd = e / (P / 8), t8 = e % (P / 8);
             const half8 x = *reinterpret_cast<const half8*>(X + (long)dd * P + 8 * t8);
 #pragma unroll
             for (int j = 0; j < 8; ++j) Xs[8 * t8 + j][dd] = x[j];
         }
-        wave_sync_lds();
+        __syncthreads();
     }
+    if (wv == 0) {
+        floatx16 acc = floatx16{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        half8 x;
-        if (dim_major) {
-            x = *reinterpret_cast<const half8*>(&Xs[l & 31][16 * kk + 8 * (l >> 5)]);
-        } else {
-            x = *reinterpret_cast<const half8*>(X + (long)(l & 31) * D + 16 * kk + 8 * (l >> 5));
-            *reinterpret_cast<half8*>(&Xs[l & 31][16 * kk + 8 * (l >> 5)]) = x;
+        for (int kk = 0; kk < D / 16; ++kk) {
+            half8 x;
+            if (dim_major) {
+                x = *reinterpret_cast<const half8*>(&Xs[l & 31][16 * kk + 8 * (l >> 5)]);
+            } else {
+                x = *reinterpret_cast<const half8*>(X + (long)(l & 31) * D + 16 * kk + 8 * (l >> 5));
+                *reinterpret_cast<half8*>(&Xs[l & 31][16 * kk + 8 * (l >> 5)]) = x;
+            }
+            acc = mfma32(x, x, acc);
         }
-        acc = mfma32(x, x, acc);
-    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Gb[0][8 * (i / 4) + 4 * (l >> 5) + (i % 4)][l & 31] = acc[i];
-    for (int e = l; e < P * P; e += 64) Vb[0][e / P][e % P] = (e / P == e % P) ? 1.0f : 0.0f;
-    wave_sync_lds();
+        for (int i = 0; i < 16; ++i) Gb[0][8 * (i / 4) + 4 * (l >> 5) + (i % 4)][l & 31] = acc[i];
+    }
+    for (int e = tid; e < P * P; e += 256) Vb[0][e / P][e % P] = (e / P == e % P) ? 1.0f : 0.0f;
+    __syncthreads();
+    // every wave forms the same trace
     float tr = l < P ? Gb[0][l][l] : 0.0f;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o, kWave);
     const float thr = 1e-6f * tr;
 
-    // ---- cyclic Jacobi. Round: lanes k < 16 form the rotation of positions
+    // ---- cyclic Jacobi. Round: threads k < 16 form the rotation of positions
     // (2k, 2k+1); then G <- J^T G J and V <- V J in one pass of 2x2 blocks, each
     // result written at its position for the next round (sigma) in the other
-    // buffer. Lane l owns the blocks (pair a = l / 4) x (pairs 4 (l % 4) + j) and
-    // the eigenvector rows l / 16 + 4 i of pair l % 16: fixed addresses.
-    const int pa = l >> 2, pv = l & 15;
+    // buffer. Thread t owns the block (pair t / 16) x (pair t % 16) and the
+    // eigenvector rows t / 16 and t / 16 + 16 of pair t % 16: fixed addresses.
+    const int pa = tid >> 4, pb = tid & 15, pv = tid & 15, vr = tid >> 4;
     const int ra0 = sigma(2 * pa), ra1 = sigma(2 * pa + 1);
-    const int cv0 = sigma(2 * pv), cv1 = sigma(2 * pv + 1);
+    const int cb0 = sigma(2 * pb), cb1 = sigma(2 * pb + 1);
     int cur = 0;
     for (int sweep = 0; sweep < a.max_sweeps; ++sweep) {
         int rotated = 0;
@@ -153,8 +151,9 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
             float (*Gn)[LD] = Gb[cur ^ 1];
             float (*V)[LD] = Vb[cur];
             float (*Vn)[LD] = Vb[cur ^ 1];
-            if (l < 16) {
-                const float gpp = G[2 * l][2 * l], gqq = G[2 * l + 1][2 * l + 1], apq = G[2 * l][2 * l + 1];
+            if (tid < 16) {
+                const float gpp = G[2 * tid][2 * tid], gqq = G[2 * tid + 1][2 * tid + 1];
+                const float apq = G[2 * tid][2 * tid + 1];
                 float c = 1.0f, s = 0.0f;
                 if (fabsf(apq) > thr) {
                     const float tau = (gqq - gpp) * __builtin_amdgcn_rcpf(2.0f * apq);
@@ -163,43 +162,39 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
                     s = t * c;
                     rotated = 1;
                 }
-                rot[l][0] = c;
-                rot[l][1] = s;
+                rot[tid][0] = c;
+                rot[tid][1] = s;
             }
-            wave_sync_lds();
-            const float ca = rot[pa][0], sa = rot[pa][1];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int pb = 4 * (l & 3) + j;
-                const float cb = rot[pb][0], sb = rot[pb][1];
+            __syncthreads();
+            {
+                const float ca = rot[pa][0], sa = rot[pa][1], cb = rot[pb][0], sb = rot[pb][1];
                 const float g00 = G[2 * pa][2 * pb], g01 = G[2 * pa][2 * pb + 1];
                 const float g10 = G[2 * pa + 1][2 * pb], g11 = G[2 * pa + 1][2 * pb + 1];
                 const float r00 = fmaf(ca, g00, -sa * g10), r01 = fmaf(ca, g01, -sa * g11);
                 const float r10 = fmaf(sa, g00, ca * g10), r11 = fmaf(sa, g01, ca * g11);
                 float n01 = fmaf(sb, r00, cb * r01), n10 = fmaf(cb, r10, -sb * r11);
                 if (pa == pb && sa != 0.0f) n01 = n10 = 0.0f;   // the pair's own entry is annihilated
-                const int cb0 = sigma(2 * pb), cb1 = sigma(2 * pb + 1);
                 Gn[ra0][cb0] = fmaf(cb, r00, -sb * r01);
                 Gn[ra0][cb1] = n01;
                 Gn[ra1][cb0] = n10;
                 Gn[ra1][cb1] = fmaf(sb, r10, cb * r11);
-            }
-            const float cv = rot[pv][0], sv = rot[pv][1];
+                const float cv = cb, sv = sb;            // pv == pb
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = (l >> 4) + 4 * i;
-                const float vp = V[row][2 * pv], vq = V[row][2 * pv + 1];
-                Vn[row][cv0] = fmaf(cv, vp, -sv * vq);
-                Vn[row][cv1] = fmaf(sv, vp, cv * vq);
+                for (int i = 0; i < 2; ++i) {
+                    const int row = vr + 16 * i;
+                    const float vp = V[row][2 * pv], vq = V[row][2 * pv + 1];
+                    Vn[row][cb0] = fmaf(cv, vp, -sv * vq);
+                    Vn[row][cb1] = fmaf(sv, vp, cv * vq);
+                }
             }
-            wave_sync_lds();
+            __syncthreads();
             cur ^= 1;
         }
-        if (!__any(rotated)) break;
-        // off-diagonal Frobenius norm of G after the sweep (lane l: rows l / 2, columns
-        // of half l % 2), against 1e-4 trace(G)
-        float off = 0.0f;
-        {
+        if (!__syncthreads_or(rotated)) break;
+        // off-diagonal Frobenius norm of G after the sweep, against 1e-4 trace(G):
+        // wave 0 sums it (lane l: row l / 2, columns of half l % 2) and decides
+        if (wv == 0) {
+            float off = 0.0f;
             float (*Gc)[LD] = Gb[cur];
             const int row = l >> 1, c0 = 16 * (l & 1);
 #pragma unroll
@@ -207,26 +202,28 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
                 const float v = Gc[row][c0 + j];
                 off = c0 + j == row ? off : fmaf(v, v, off);
             }
-        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o, kWave);
-        if (off <= 1e-8f * tr * tr) break;
+            for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o, kWave);
+            if (l == 0) stop = off <= 1e-8f * tr * tr;
+        }
+        __syncthreads();
+        if (stop) break;
     }
     float (*G)[LD] = Gb[cur];
     float (*V)[LD] = Vb[cur];
     float (*Ls)[LD] = Gb[cur ^ 1];     // free now: L^T [k][t] as rounded to fp16
 
     // ---- descending eigen-order, ties towards the lower index
-    if (l < P) {
-        const float li = G[l][l];
+    if (tid < P) {
+        const float li = G[tid][tid];
         int rank = 0;
         for (int j = 0; j < P; ++j) {
             const float lj = G[j][j];
-            rank += (lj > li) || (lj == li && j < l);
+            rank += (lj > li) || (lj == li && j < tid);
         }
-        order[rank] = l;
+        order[rank] = tid;
     }
-    wave_sync_lds();
+    __syncthreads();
 
     const long bh = (long)b * a.H + h;
     const long page = bh * a.max_pages + pg;
@@ -234,34 +231,24 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
         half_t* Lo = (is_v ? a.lv : a.lk) + page * P * r;
         half_t* Ro = (is_v ? a.rv : a.rk) + page * (long)r * D;
         // keys: L [P][r], R [r][D]; values transposed: L^T [r][P], R^T [D][r]
-        for (int e = l; e < P * r; e += 64) {
+        for (int e = tid; e < P * r; e += 256) {
             const int t = e / r, k = e % r;
             const half_t v = (half_t)V[t][order[k]];
             Lo[is_v ? k * P + t : e] = v;
             Ls[k][t] = (float)v;
         }
-        wave_sync_lds();
-        // R[k][d] = sum_t fp16(L[t][k]) X[t][d]: lane l owns dims l and l + 64
-        float x0[P], x1[P];
+        __syncthreads();
+        // R[k][d] = sum_t fp16(L[t][k]) X[t][d]: thread d < D owns dim d
+        if (tid < D) {
+            float x0[P];
 #pragma unroll
-        for (int t = 0; t < P; ++t) {
-            x0[t] = (float)Xs[t][l];
-            x1[t] = (float)Xs[t][l + 64];
-        }
-        for (int k = 0; k < r; ++k) {
-            float s0 = 0.0f, s1 = 0.0f;
+            for (int t = 0; t < P; ++t) x0[t] = (float)Xs[t][tid];
+            for (int k = 0; k < r; ++k) {
+                float s0 = 0.0f;
 #pragma unroll
-            for (int t = 0; t < P; ++t) {
-                const float lt = Ls[k][t];
-                s0 = fmaf(lt, x0[t], s0);
-                s1 = fmaf(lt, x1[t], s1);
-            }
-            if (is_v) {
-                Ro[(long)l * r + k] = (half_t)s0;
-                Ro[(long)(l + 64) * r + k] = (half_t)s1;
-            } else {
-                Ro[(long)k * D + l] = (half_t)s0;
-                Ro[(long)k * D + l + 64] = (half_t)s1;
+                for (int t = 0; t < P; ++t) s0 = fmaf(Ls[k][t], x0[t], s0);
+                if (is_v) Ro[(long)tid * r + k] = (half_t)s0;
+                else Ro[(long)k * D + tid] = (half_t)s0;
             }
         }
         return;
@@ -295,55 +282,47 @@ __global__ __launch_bounds__(64) void factor_pages(const FactorArgs a) {
             for (int n = 0; n < 32; ++n) deq[n] = (float)c[n] * (float)sc;
         }
     };
-    if (l < P * r / 32) {
+    if (tid < P * r / 32) {
         float x[32], xd[32];
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
-            const int e = 32 * l + n;
+            const int e = 32 * tid + n;
             const int t = is_v ? e % P : e / r, k = is_v ? e / P : e % r;
             x[n] = V[t][order[k]];
         }
-        store_group(Lc, Lsc, l, x, xd);
+        store_group(Lc, Lsc, tid, x, xd);
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
-            const int e = 32 * l + n;
+            const int e = 32 * tid + n;
             const int t = is_v ? e % P : e / r, k = is_v ? e / P : e % r;
             Ls[k][t] = xd[n];
         }
     }
-    wave_sync_lds();
+    __syncthreads();
     // R (fp32) [r][D] into the eigenvector buffers, which are free now
     float* Rs = &Vb[0][0][0];
-    {
-        float x0[P], x1[P];
+    if (tid < D) {
+        float x0[P];
 #pragma unroll
-        for (int t = 0; t < P; ++t) {
-            x0[t] = (float)Xs[t][l];
-            x1[t] = (float)Xs[t][l + 64];
-        }
+        for (int t = 0; t < P; ++t) x0[t] = (float)Xs[t][tid];
         for (int k = 0; k < r; ++k) {
-            float s0 = 0.0f, s1 = 0.0f;
+            float s0 = 0.0f;
 #pragma unroll
-            for (int t = 0; t < P; ++t) {
-                const float lt = Ls[k][t];
-                s0 = fmaf(lt, x0[t], s0);
-                s1 = fmaf(lt, x1[t], s1);
-            }
-            Rs[k * D + l] = s0;
-            Rs[k * D + l + 64] = s1;
+            for (int t = 0; t < P; ++t) s0 = fmaf(Ls[k][t], x0[t], s0);
+            Rs[k * D + tid] = s0;
         }
     }
-    wave_sync_lds();
-    if (l < r * D / 32) {
+    __syncthreads();
+    if (tid < r * D / 32) {
         float x[32];
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
-            const int e = 32 * l + n;
+            const int e = 32 * tid + n;
             // keys R [r][D]; values in rank quads, [r/4][D][4]
             const int k = is_v ? 4 * (e / (4 * D)) + e % 4 : e / D, d = is_v ? (e / 4) % D : e % D;
             x[n] = Rs[k * D + d];
         }
-        store_group(Rc, Rsc, l, x, nullptr);
+        store_group(Rc, Rsc, tid, x, nullptr);
     }
 }
 
@@ -369,7 +348,7 @@ int32_t launch_factor_page(const lrkv_paged_cache* c, const int32_t* pages, int 
                  pages, n_pages, c->batch, c->kv_heads, c->page_size, c->sink_pages,
                  c->window_pages, c->max_pages, c->rank_k, c->rank_v, src_len, max_sweeps,
                  c->factor_fmt == LRKV_FMT_INT4_G32};
-    hipLaunchKernelGGL(factor_pages<128>, dim3(2 * n_pages), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(factor_pages<128>, dim3(2 * n_pages), dim3(256), 0, st, a);
     hipLaunchKernelGGL(mark_factored, dim3((n_pages + 255) / 256), dim3(256), 0, st, a);
     return last_launch_status();
 }
