@@ -255,10 +255,12 @@ int32_t lrkv_decode_attn(int32_t mode, const void *cache, const float *q, const 
  * Defined by: the two calls it combines (Palu digest, Method details: new
  * tokens enter the cache as latents, then the query attends over all of them).
  *
- * With the RoPE mode, fp16 latents and at most 1024 new 8-element rows
- * (batch * units * n_new * rank / 8) the append runs inside the query
- * preparation's launch and lens advances in the merge's: three launches instead
- * of four. Other modes and formats enqueue the append and the decode in turn.
+ * With the RoPE mode and a decode-size append (fp16: at most 1024 new 8-element
+ * rows, batch * units * n_new * rank / 8; int4: at most 1024 key groups plus
+ * value token-pair groups, batch * units * (n_new + n_new / 2 + 2) * rank / 32)
+ * the append runs inside the query preparation's launch and lens advances in
+ * the merge's: three launches instead of four (six with int4). Other modes and
+ * sizes enqueue the append and the decode in turn.
  *
  * Errors: those of the two calls; every check of both is made before anything
  * is enqueued, so a rejected call leaves the cache, lens and out unchanged.

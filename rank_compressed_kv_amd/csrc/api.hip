@@ -293,7 +293,7 @@ int32_t lrkv_decode_step(int32_t mode, const void* cache, const void* new_k, con
     if (!workspace || ws_bytes < need || !aligned16(workspace)) return LRKV_ERR_WORKSPACE;
     if (mode == LRKV_MODE_ROPE_RECON) {
         const lrkv_latent_cache* c = (const lrkv_latent_cache*)cache;
-        if (c->fmt == LRKV_FMT_FP16 && (long)c->batch * c->units * n_new * (c->rank / 8) <= kSmallAppendRows) {
+        if (fused_append_fits(c, n_new)) {
             const FusedAppend app{(const float*)new_k, (const float*)new_v, n_new};
             return decode_common(mode, kPhaseAll, cache, q, bk, q_pos, sm_scale, out, workspace, ws_bytes,
                                  len_after, n_split, stream, nullptr, &app);

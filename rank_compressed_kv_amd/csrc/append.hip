@@ -67,33 +67,8 @@ __global__ __launch_bounds__(256) void append_fp16_small(const float* __restrict
 __global__ void append_int4_k(const float* __restrict__ nk, uint8_t* __restrict__ hk,
                               half_t* __restrict__ sk, const int32_t* __restrict__ lens, int B,
                               int U, int r, int cap, int n_new) {
-    const int G = r / 32;
-    const long total = (long)B * U * n_new * G;
-    long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= total) return;
-    const int g = (int)(e % G);
-    long rest = e / G;
-    const int i = (int)(rest % n_new);
-    rest /= n_new;
-    const int u = (int)(rest % U);
-    const int b = (int)(rest / U);
-    const int pos = lens[b] + i;
-    if (pos >= cap) return;
-    const float* x = nk + ((((long)b * U + u) * n_new + i) * r + g * 32);
-    int codes[32];
-    half_t s16;
-    quant_group(x, codes, &s16);
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc |= (uint32_t)(codes[q * 8 + k] & 0xF) << (4 * k);
-        w[q] = acc;
-    }
-    const long bu = (long)b * U + u;
-    *reinterpret_cast<uint4*>(hk + (bu * cap + pos) * (r / 2) + g * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    sk[(bu * cap + pos) * G + g] = s16;
+    const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < (long)B * U * n_new * (r / 32)) append_int4_key_group(nk, hk, sk, lens, B, U, r, cap, n_new, e);
 }
 
 // Values: one thread per (b, u, token pair, group) so that no two threads share a
@@ -101,43 +76,9 @@ __global__ void append_int4_k(const float* __restrict__ nk, uint8_t* __restrict_
 __global__ void append_int4_v(const float* __restrict__ nv, uint8_t* __restrict__ hv,
                               half_t* __restrict__ sv, const int32_t* __restrict__ lens, int B,
                               int U, int r, int cap, int n_new) {
-    const int G = r / 32;
-    const int n_pairs = n_new / 2 + 2;       // pairs touched by [len, len + n_new)
-    const long total = (long)B * U * n_pairs * G;
-    long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= total) return;
-    const int g = (int)(e % G);
-    long rest = e / G;
-    const int pi = (int)(rest % n_pairs);
-    rest /= n_pairs;
-    const int u = (int)(rest % U);
-    const int b = (int)(rest / U);
-    const int len = lens[b];
-    const int pair = len / 2 + pi;           // covers tokens 2*pair, 2*pair + 1
-    const long bu = (long)b * U + u;
-    int codes[2][32];
-    bool own[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int pos = 2 * pair + h;
-        own[h] = pos >= len && pos < len + n_new && pos < cap;
-        if (own[h]) {
-            half_t s16;
-            quant_group(nv + ((bu * n_new + (pos - len)) * r + g * 32), codes[h], &s16);
-            sv[((bu * (cap / kTile) + pos / kTile) * G + g) * kTile + pos % kTile] = s16;
-        }
-    }
-    if (!own[0] && !own[1]) return;
-    const int pos0 = 2 * pair;
-    uint8_t* base = hv + ((bu * (cap / kTile) + pos0 / kTile) * r + g * 32) * (kTile / 2) + (pos0 % kTile) / 2;
-#pragma unroll 4
-    for (int k = 0; k < 32; ++k) {
-        uint8_t* p = base + k * (kTile / 2);
-        uint32_t byte = own[0] && own[1] ? 0u : (uint32_t)*p;
-        if (own[0]) byte = (byte & 0xF0u) | ((uint32_t)codes[0][k] & 0xFu);
-        if (own[1]) byte = (byte & 0x0Fu) | (((uint32_t)codes[1][k] & 0xFu) << 4);
-        *p = (uint8_t)byte;
-    }
+    const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < (long)B * U * (n_new / 2 + 2) * (r / 32))
+        append_int4_value_pair(nv, hv, sv, lens, B, U, r, cap, n_new, e);
 }
 
 // Hybrid cache: one thread per (b, h, i, 8 dims) copying K and V into the dense

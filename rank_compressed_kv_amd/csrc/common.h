@@ -18,9 +18,9 @@ constexpr int kWave = 64;
 constexpr int kTile = 32;          // tokens per attention tile == cache block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplit = 1024;    // sequence chunks merged per head (merge kernel's LDS)
-// A decode-size fp16 append runs in one workgroup of 256 threads (and inside the
-// query preparation of lrkv_decode_step) when it has at most this many 8-element
-// rows (B * U * n_new * r / 8).
+// A decode-size append runs in one workgroup of 256 threads (and inside the query
+// preparation of lrkv_decode_step) when it has at most this many items: fp16
+// 8-element rows, or int4 key groups plus value token-pair groups.
 constexpr int kSmallAppendRows = 1024;
 constexpr int kMaxRopeTiles = 256; // tiles per RoPE chunk: bounds the angle-rotation drift
 
@@ -129,6 +129,14 @@ struct FusedAppend {
     const float* nv;
     int n_new;
 };
+// Whether an append of n_new tokens fits the one-workgroup append role of the
+// query preparation: fp16 rows of 8 elements, or int4 key groups plus value
+// token-pair groups, at most kSmallAppendRows items.
+inline bool fused_append_fits(const lrkv_latent_cache* c, int n_new) {
+    const long bu = (long)c->batch * c->units;
+    if (c->fmt == LRKV_FMT_FP16) return bu * n_new * (c->rank / 8) <= kSmallAppendRows;
+    return bu * (n_new + n_new / 2 + 2) * (c->rank / 32) <= kSmallAppendRows;
+}
 // Validation and dispatch shared by every decode entry point (api.hip). With
 // ws_need non-null it only validates and stores the workspace size needed.
 int32_t decode_common(int32_t mode, int phases, const void* cache, const float* q, const void* bk,

@@ -11,7 +11,7 @@ void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, co
                       half_t* qp, float* qs, float2* angles, int B, int U, int s, int gq, int DH,
                       int R, int n_split, int chunk, double theta, float scale, int qmode,
                       bool int4, hipStream_t st, int pending, const float* nk, const float* nv,
-                      half_t* hk, half_t* hv, int cap);
+                      void* hk, void* hv, half_t* sk, half_t* sv, int cap);
 int32_t launch_rope_decode(const lrkv_latent_cache* c, const half_t* qp, const float* qs,
                            const float2* angles, float* part, int n_split, int chunk, hipStream_t st,
                            int pending);
@@ -49,7 +49,8 @@ int32_t launch_decode_latent(int mode, int phases, const lrkv_latent_cache* c, c
             launch_rope_prep(q, bk, q_pos, c->lens, qp, qs, angles, g.B, g.U, g.s, g.gq, g.dh, g.r,
                              w.n_split, w.chunk, (double)g.theta, sm_scale * kLog2e, qmode,
                              g.fmt == LRKV_FMT_INT4_G32, st, pending, app ? app->nk : nullptr,
-                             app ? app->nv : nullptr, (half_t*)c->hk, (half_t*)c->hv, c->capacity);
+                             app ? app->nv : nullptr, c->hk, c->hv, (half_t*)c->sk, (half_t*)c->sv,
+                             c->capacity);
         if (phases & kPhasePartials) {
             const int32_t rc = gqa ? launch_rope_gqa(c, qp, angles, part, w.n_split, w.chunk, st, pending)
                                    : launch_rope_decode(c, qp, qs, angles, part, w.n_split, w.chunk, st,

@@ -43,10 +43,12 @@ struct PrepArgs {
     int qmode, int4;
     int n_q, n_s;            // blocks of the Q' / B^k role and of the query-scaling role
     // fused append (lrkv_decode_step): n_app = 1 block writes the `pending` new
-    // tokens (nk, nv [B][U][pending][R] fp32) into hk / hv
-    int n_app, pending, cap;
+    // tokens (nk, nv [B][U][pending][R] fp32) into the cache (fp16 latents, or
+    // int4 codes with their scales sk / sv)
+    int n_app, pending, cap, app_int4;
     const float *nk, *nv;
-    half_t *hk, *hv;
+    void *hk, *hv;
+    half_t *sk, *sv;
 };
 
 __device__ __forceinline__ size_t qp_index(bool frag, int bu, int NH, int h, int DH, int R, int row, int k) {
@@ -233,7 +235,17 @@ __device__ void prep_angles(const PrepArgs& a, int blk) {
 
 __global__ __launch_bounds__(256) void rope_prepare(const PrepArgs a) {
     if ((int)blockIdx.x < a.n_app) {
-        append_fp16_rows(a.nk, a.nv, a.hk, a.hv, a.lens, a.B, a.U, a.R, a.cap, a.pending, threadIdx.x, 256);
+        if (!a.app_int4) {
+            append_fp16_rows(a.nk, a.nv, (half_t*)a.hk, (half_t*)a.hv, a.lens, a.B, a.U, a.R, a.cap, a.pending,
+                             threadIdx.x, 256);
+        } else {
+            const long n_keys = (long)a.B * a.U * a.pending * (a.R / 32);
+            const long n_vals = (long)a.B * a.U * (a.pending / 2 + 2) * (a.R / 32);
+            for (long e = threadIdx.x; e < n_keys; e += 256)
+                append_int4_key_group(a.nk, (uint8_t*)a.hk, a.sk, a.lens, a.B, a.U, a.R, a.cap, a.pending, e);
+            for (long e = threadIdx.x; e < n_vals; e += 256)
+                append_int4_value_pair(a.nv, (uint8_t*)a.hv, a.sv, a.lens, a.B, a.U, a.R, a.cap, a.pending, e);
+        }
         return;
     }
     const int blk = blockIdx.x - a.n_app;
@@ -253,9 +265,9 @@ void launch_rope_prep(const float* q, const half_t* bk, const int32_t* q_pos, co
                       half_t* qp, float* qs, float2* angles, int B, int U, int s, int gq, int DH,
                       int R, int n_split, int chunk, double theta, float scale, int qmode,
                       bool int4, hipStream_t st, int pending, const float* nk, const float* nv,
-                      half_t* hk, half_t* hv, int cap) {
+                      void* hk, void* hv, half_t* sk, half_t* sv, int cap) {
     PrepArgs a{q, bk, q_pos, lens, qp, qs, angles, B, U, s, gq, DH, R, n_split, chunk, theta, scale,
-               qmode, int4 ? 1 : 0, 0, 0, nk ? 1 : 0, pending, cap, nk, nv, hk, hv};
+               qmode, int4 ? 1 : 0, 0, 0, nk ? 1 : 0, pending, cap, int4 ? 1 : 0, nk, nv, hk, hv, sk, sv};
     if (qmode == kQpGqaFragments) {
         a.n_q = (int)(((long)U * 128 * R + 255) / 256);
         a.n_s = (int)(((long)B * U * s * gq * DH + 255) / 256);
