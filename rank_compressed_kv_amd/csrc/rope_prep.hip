@@ -239,12 +239,17 @@ __global__ __launch_bounds__(256) void rope_prepare(const PrepArgs a) {
             append_fp16_rows(a.nk, a.nv, (half_t*)a.hk, (half_t*)a.hv, a.lens, a.B, a.U, a.R, a.cap, a.pending,
                              threadIdx.x, 256);
         } else {
+            // key groups and value pairs on different threads (independent items), so
+            // that the two chains of loads and stores run side by side
             const long n_keys = (long)a.B * a.U * a.pending * (a.R / 32);
             const long n_vals = (long)a.B * a.U * (a.pending / 2 + 2) * (a.R / 32);
-            for (long e = threadIdx.x; e < n_keys; e += 256)
-                append_int4_key_group(a.nk, (uint8_t*)a.hk, a.sk, a.lens, a.B, a.U, a.R, a.cap, a.pending, e);
-            for (long e = threadIdx.x; e < n_vals; e += 256)
-                append_int4_value_pair(a.nv, (uint8_t*)a.hv, a.sv, a.lens, a.B, a.U, a.R, a.cap, a.pending, e);
+            for (long e = threadIdx.x; e < n_keys + n_vals; e += 256) {
+                if (e < n_keys)
+                    append_int4_key_group(a.nk, (uint8_t*)a.hk, a.sk, a.lens, a.B, a.U, a.R, a.cap, a.pending, e);
+                else
+                    append_int4_value_pair(a.nv, (uint8_t*)a.hv, a.sv, a.lens, a.B, a.U, a.R, a.cap, a.pending,
+                                           e - n_keys);
+            }
         }
         return;
     }
