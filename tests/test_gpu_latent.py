@@ -113,6 +113,13 @@ def test_append_int4_bitexact():
         k[0, 1, 0, 7] = -3.0                                           # single nonzero
         k[1, 0, 0, :32] = np.float32(1.0) * np.array([7.0] + [2.5, 3.5, -2.5, 0.5] * 7 + [1.5, 6.5, -6.5], np.float32)
         v[1, 1, 0, 32:] = np.array([7.0] + [(k + 0.5) for k in range(-4, 3)] * 4 + [0.5, 1.5, -0.5], np.float32)
+        # exact ties of an inexact scale: amax 1 -> s16 = fp16(fp32(1) / 7), x = s16 (k + 1/2)
+        s16 = np.float64(np.float16(np.float32(1.0) / np.float32(7.0)))
+        ties = np.array([1.0] + [s16 * (j + 0.5) for j in (0, 1, 2, 3, -1, -4, -2, -3)] * 3
+                        + [s16 * 4.5, -s16 * 5.5, s16 * 6.5, -s16 * 6.5, s16 * 5.5, -s16 * 0.5, s16 * 1.5],
+                        np.float32)
+        k[1, 1, 0, 32:] = ties
+        v[0, 0, 0, :32] = -ties
         cache.append(to_dev(k), to_dev(v))
         ks.append(k)
         vs.append(v)
