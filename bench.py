@@ -327,7 +327,32 @@ def measure_rows(torch, lrkv, dev) -> dict:
     rows["rope_int4_gqa_B4_T65536"] = _row(torch, fns, B4 * H4 * T4 * 72,
                                            B4 * H4 * T4 * (2 * R4 * DH + 2 * G4 * DH + 2 * G4 * R4),
                                            replica_bytes=_latent_bytes(c))
-    del c, reps, q4, bk4, wss, out, fns
+    # the whole step on the same caches: one token appended (int4, fused into the
+    # query preparation) and decoded, one lrkv_decode_step call. Each call grows
+    # its replica by one token; lengths start 256 below T4 (the tokens there are
+    # overwritten) and stay within [T4 - 256, T4 - 256 + len_growth], so every
+    # chunk keeps the decode row's 32 tiles
+    nk4 = torch.randn((64, B4, H4, 1, R4), generator=g, device=dev) * s4
+    nv4 = torch.randn((64, B4, H4, 1, R4), generator=g, device=dev) * s4
+    for r in reps:
+        r.host_lens[:] = T4 - 256
+        r.lens.fill_(T4 - 256)
+    wss = [r.workspace(lrkv.MODE_ROPE_RECON) for r in reps]   # valid up to length T4
+    n_calls = [0]
+
+    def step4(r, w):
+        i = n_calls[0] % 64
+        n_calls[0] += 1
+        lrkv.decode_step(lrkv.MODE_ROPE_RECON, r.desc, nk4[i], nv4[i], 1, q4, bk4, None, 0.0, out, w, r.max_len)
+        r.host_lens += 1
+
+    fns = [lambda r=r, w=w: step4(r, w) for r, w in zip(reps, wss)]
+    row = _row(torch, fns, B4 * H4 * T4 * 72, B4 * H4 * T4 * (2 * R4 * DH + 2 * G4 * DH + 2 * G4 * R4),
+               replica_bytes=_latent_bytes(c))
+    row["len_growth"] = int(max(r.max_len for r in reps)) - (T4 - 256)
+    assert row["len_growth"] <= 256
+    rows["rope_int4_gqa_step_B4_T65536"] = row
+    del c, reps, q4, bk4, wss, out, fns, nk4, nv4
 
     # PuzzleKV hybrid: Llama-3.1-8B shape, batch 8, T = 32K, rank-12 pages
     g.manual_seed(5)
