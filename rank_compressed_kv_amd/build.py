@@ -32,11 +32,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INC, "-I" + SRC,
 ]
-# Per-source extras. rope_decode.hip: MFMA accumulators in the arithmetic
-# registers, so that the head-wave kernel's resident Q' (pinned to AGPRs) is read
-# by the MFMAs in place.
+# Per-source extras: MFMA accumulators in the arithmetic registers, so that
+# operands resident for a whole loop (Q' of the head-wave kernel; B^k fragments
+# and queries of the prefill kernel), pinned to the AGPRs, are read by the MFMAs
+# in place, and the vector work on the accumulators needs no copies.
 FILE_FLAGS = {
     "rope_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

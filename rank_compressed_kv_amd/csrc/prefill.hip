@@ -16,11 +16,12 @@
 //                                lane holds both halves of each rotated pair;
 //   RoPE at each token's position in registers, (cos, sin) = tile start x
 //   in-tile offset (both fp64-reduced by the prepare kernel); K written to LDS
-//   as fp16 hi + lo;
+//   in fp16 (queries too: the fp16 rounding of p for the value product already
+//   bounds the output error, and splitting K and q into hi + lo pairs was
+//   measured to change it by less than 15%);
 //   S^T [token][row] = K Q^T     16x16x32 MFMA, wave w owning 32 query rows,
 //                                rows of K permuted so that a lane's output is 8
-//                                consecutive tokens of one query row; hi x hi,
-//                                hi x lo, lo x hi;
+//                                consecutive tokens of one query row;
 //   causal mask, online softmax (log2 domain; queries pre-scaled);
 //   O^T [dim][row] += V^T P^T    16x16x32 MFMA over the dim-major value block.
 // Key and value tiles go buffer->LDS, one tile ahead; two barriers per tile.
@@ -118,8 +119,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
     static_assert(R == 256, "prefill kernel covers rank 256");
     __shared__ __attribute__((aligned(1024))) half_t htile[2][32 * R];    // H^k [token][rank], chunks swizzled
     __shared__ __attribute__((aligned(1024))) half_t vtile[2][R * 32];    // H^v [rank][token], chunks swizzled
-    __shared__ __attribute__((aligned(16))) half_t krot[2][32 * DH];      // K hi, lo [token][dim], chunks swizzled
-    __shared__ float2 tokb[32][DH / 2];                                   // (cos, sin)(tau theta_f), tau < 32
+    __shared__ __attribute__((aligned(16))) half_t krot[32 * DH];         // K [token][dim], chunks swizzled
+    __shared__ float2 tokb[DH / 2][32];                                   // (cos, sin)(tau theta_f), tau < 32
 
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int c = l & 15, g = l >> 4;
@@ -202,8 +203,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) bf[ks][e] = col[(long)(16 * ks + 8 * (l >> 5) + e) * (a.s * DH)];
     }
-    // queries of the lane's rows, dims 32 ks + 8 g + e, as fp16 hi + lo
-    half8 qh[NRB][4], ql[NRB][4];
+    // queries of the lane's rows, dims 32 ks + 8 g + e, in fp16
+    half8 qh[NRB][4];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
         const float* qs = a.qr + ((long)(b * a.M + m_row[rb]) * Hq + j_row[rb]) * DH;
@@ -211,14 +212,14 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = row_ok[rb] ? qs[32 * ks + 8 * g + e] : 0.0f;
-                qh[rb][ks][e] = (half_t)v;
-                ql[rb][ks][e] = (half_t)(v - (float)qh[rb][ks][e]);
+                qh[rb][ks][e] = (half_t)(row_ok[rb] ? qs[32 * ks + 8 * g + e] : 0.0f);
             }
     }
-    // in-tile offsets (cos, sin)(tau theta_f) to LDS; the lane's token is tau = l % 32
+    // in-tile offsets (cos, sin)(tau theta_f) to LDS, frequency-major (the 32 lanes
+    // of a frequency read 32 consecutive entries); the lane's token is tau = l % 32
     // and its eight frequencies f_i = 16 wv + 8 (i / 4) + 4 (l / 32) + i % 4
-    for (int e = tid; e < 32 * (DH / 2); e += 256) (&tokb[0][0])[e] = a.ang[(long)a.n_tiles * (DH / 2) + e];
+    for (int e = tid; e < 32 * (DH / 2); e += 256)
+        tokb[e % (DH / 2)][e / (DH / 2)] = a.ang[(long)a.n_tiles * (DH / 2) + e];
     auto freq = [&](int i) { return 16 * wv + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3); };
     // key fragment of the reconstruction (B operand): token l % 32, ranks 16 ks + 8 (l/32)
     auto koff = [&](int ks) { return (l & 31) * R + 8 * ((2 * (ks & 7) + (l >> 5)) ^ (l & 15)) + 128 * (ks >> 3); };
@@ -238,6 +239,15 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
     float2 st[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)t_beg * (DH / 2) + freq(i)];
+    // B^T fragments and queries stay in the AGPRs for the whole loop, where the
+    // MFMAs read them in place (the accumulators and the vector work use the
+    // arithmetic registers); pinned once every load above has been issued
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(bf[ks]));
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qh[rb][ks]));
     for (int t = t_beg; t < t_end; ++t) {
         const int t0 = 32 * t;
         // vmcnt(0) as a builtin: the compiler sees it, so it inserts no later wait for
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
         __syncthreads();                      // tile t in LDS; tile t-1 fully consumed
         if (t + 1 < t_end) issue(t + 1);
 
-        // ---- K^T for the wave's 32 dims, RoPE, K hi / lo to LDS
+        // ---- K^T for the wave's 32 dims, RoPE, K to LDS
         {
             const half_t* ht = htile[t & 1];
             floatx16 acc = floatx16{};
@@ -256,27 +266,23 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
             const int tl = l & 31;
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
-                half_t lh[4], ll[4], hh[4], hl[4];
+                half_t lh[4], hh[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * gi + e;
-                    const float2 tk = tokb[tl][freq(i)];
+                    const float2 tk = tokb[freq(i)][tl];
                     const float cc = st[i].x * tk.x - st[i].y * tk.y;
                     const float ss = st[i].x * tk.y + st[i].y * tk.x;
                     const float lo = acc[i], hi = acc[i + 8];
                     const float lo2 = lo * cc - hi * ss, hi2 = hi * cc + lo * ss;
                     lh[e] = (half_t)lo2;
-                    ll[e] = (half_t)(lo2 - (float)lh[e]);
                     hh[e] = (half_t)hi2;
-                    hl[e] = (half_t)(hi2 - (float)hh[e]);
                 }
                 // dims 16 wv + 8 gi + 4 (l/32) + e (chunk 2 wv + gi) and their partners (+64)
                 const int q_lo = (2 * wv + gi) ^ (tl & 15), q_hi = (8 + 2 * wv + gi) ^ (tl & 15);
                 const int o_lo = tl * DH + 8 * q_lo + 4 * (l >> 5), o_hi = tl * DH + 8 * q_hi + 4 * (l >> 5);
-                *reinterpret_cast<half4*>(&krot[0][o_lo]) = half4{lh[0], lh[1], lh[2], lh[3]};
-                *reinterpret_cast<half4*>(&krot[1][o_lo]) = half4{ll[0], ll[1], ll[2], ll[3]};
-                *reinterpret_cast<half4*>(&krot[0][o_hi]) = half4{hh[0], hh[1], hh[2], hh[3]};
-                *reinterpret_cast<half4*>(&krot[1][o_hi]) = half4{hl[0], hl[1], hl[2], hl[3]};
+                *reinterpret_cast<half4*>(&krot[o_lo]) = half4{lh[0], lh[1], lh[2], lh[3]};
+                *reinterpret_cast<half4*>(&krot[o_hi]) = half4{hh[0], hh[1], hh[2], hh[3]};
             }
         }
         if (t + 1 < t_end) {
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
         __syncthreads();                      // K of tile t complete
 
         // ---- S^T [token][row] for both row blocks: block mb row m is token
-        // 8 (m/4) + 4 mb + m % 4; hi x hi + hi x lo + lo x hi, four chains
+        // 8 (m/4) + 4 mb + m % 4; four chains
         floatx4 S[NRB][2];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -294,22 +300,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
             for (int mb = 0; mb < 2; ++mb) S[rb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            half8 kh[2], kl[2];
+            half8 kh[2];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const int tk = 8 * (c >> 2) + 4 * mb + (c & 3);
-                const int off = tk * DH + 8 * ((4 * ks + g) ^ (tk & 15));
-                kh[mb] = lds8(&krot[0][off]);
-                kl[mb] = lds8(&krot[1][off]);
+                kh[mb] = lds8(&krot[tk * DH + 8 * ((4 * ks + g) ^ (tk & 15))]);
             }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    S[rb][mb] = mfma16(kh[mb], qh[rb][ks], S[rb][mb]);
-                    S[rb][mb] = mfma16(kh[mb], ql[rb][ks], S[rb][mb]);
-                    S[rb][mb] = mfma16(kl[mb], qh[rb][ks], S[rb][mb]);
-                }
+                for (int mb = 0; mb < 2; ++mb) S[rb][mb] = mfma16(kh[mb], qh[rb][ks], S[rb][mb]);
         }
 
         // ---- causal mask and online softmax per row block; lane (c, g): row c at

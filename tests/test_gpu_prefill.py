@@ -48,6 +48,7 @@ def test_prefill_parity(B, U, s, gq, T0, M, cap):
     ref = oattn.palu_prefill(oattn.stored_fp16(lay["hk"]), oattn.stored_fp16(lay["hv"]),
                              bk16.astype(np.float64), q, p0, s, gq, DH, THETA)
     err = rel_l2(got.reshape(B * M, Hq, R), ref.reshape(B * M, Hq, R))
+    say(f"  max rel-L2 {err.max():.3e} (tolerance {TOL})")
     assert err.max() <= TOL, err.max()
 
 
@@ -73,6 +74,7 @@ def test_prefill_ragged_positions():
     ref = oattn.palu_prefill(oattn.stored_fp16(lay["hk"]), oattn.stored_fp16(lay["hv"]),
                              bk16.astype(np.float64), q, p0, s, gq, DH, THETA)
     err = rel_l2(got.reshape(B * M, Hq, R), ref.reshape(B * M, Hq, R))
+    say(f"  max rel-L2 {err.max():.3e} (tolerance {TOL})")
     assert err.max() <= TOL, err.max()
 
 
@@ -112,7 +114,9 @@ def test_prefill_full_size_sampled():
         hv = oattn.stored_fp16(np.concatenate(keep_v[u])[None, None, :n])
         ref = oattn.palu_decode(hk, hv, bk16[u:u + 1].astype(np.float64), q[:, m, u * s * gq:(u + 1) * s * gq],
                                 [n], s, gq, DH, THETA)
-        assert rel_l2(got[0, m, j], ref[0, j - u * s * gq]) <= TOL, (m, j)
+        err = rel_l2(got[0, m, j], ref[0, j - u * s * gq])
+        say(f"  row {m} head {j}: rel-L2 {err:.3e} (tolerance {TOL})")
+        assert err <= TOL, (m, j)
 
 
 def test_prefill_without_rope():
@@ -131,4 +135,5 @@ def test_prefill_without_rope():
     ref = oattn.palu_prefill(oattn.stored_fp16(lay["hk"]), oattn.stored_fp16(lay["hv"]),
                              bk16.astype(np.float64), q, p0, s, gq, DH, 0.0)
     err = rel_l2(got.reshape(B * M, Hq, R), ref.reshape(B * M, Hq, R))
+    say(f"  max rel-L2 {err.max():.3e} (tolerance {TOL})")
     assert err.max() <= TOL, err.max()
