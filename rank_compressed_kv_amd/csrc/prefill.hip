@@ -28,6 +28,7 @@
 #include "tiles.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace lrkv {
 namespace {
@@ -150,6 +151,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
         j_row[rb] = (u * a.s + w) * a.gq + (row_ok[rb] ? rho % a.gq : 0);
         pos[rb] = row_ok[rb] ? qpos(a.p0, a.lens, b, m_row[rb]) : -1;
     }
+    // the wave's smallest row position (-1 if it holds a row past the chunk): key
+    // tiles ending at or before it are visible to all of the wave's rows
+    int pos_min = min(pos[0], pos[1]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o, kWave));
+    pos_min = __builtin_amdgcn_readfirstlane(pos_min);
     const int m_last = (min(rows, row0 + 128) - 1) / a.gq;
     const int n_t = min(a.n_tiles, qpos(a.p0, a.lens, b, m_last) / 32 + 1);
     const int t_beg = sp * a.tps, t_end = min(n_t, t_beg + a.tps);
@@ -313,35 +320,49 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
         }
 
         // ---- causal mask and online softmax per row block; lane (c, g): row c at
-        // tokens t0 + 8 g + jj, jj = 4 mb + i
+        // tokens t0 + 8 g + jj, jj = 4 mb + i. A tile that every row of the wave
+        // sees whole (FULL) needs no mask, and its maxima are finite, so the
+        // guards against -inf - -inf drop out too (exp2(-inf) is 0).
         half8 pb[NRB];
+        float alpha[NRB];
+        bool moved[NRB];
+        auto softmax = [&](auto full_c) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            float sv[8];
+            for (int rb = 0; rb < NRB; ++rb) {
+                float sv[8];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float v = S[rb][jj >> 2][jj & 3];
-                sv[jj] = t0 + 8 * g + jj <= pos[rb] ? v : -INFINITY;
+                for (int jj = 0; jj < 8; ++jj) {
+                    const float v = S[rb][jj >> 2][jj & 3];
+                    sv[jj] = FULL || t0 + 8 * g + jj <= pos[rb] ? v : -INFINITY;
+                }
+                float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                 fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+                mx = col_max(mx);
+                const float mn = fmaxf(m_run[rb], mx);
+                moved[rb] = __builtin_amdgcn_ballot_w64(mn > m_run[rb]) != 0;
+                alpha[rb] = !moved[rb] ? 1.0f
+                          : !FULL && m_run[rb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
+                m_run[rb] = mn;
+                float psum = 0.0f;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const float pv = !FULL && sv[jj] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[jj] - mn);
+                    psum += pv;
+                    pb[rb][jj] = (half_t)pv;
+                }
+                l_lane[rb] = fmaf(l_lane[rb], alpha[rb], psum);
             }
-            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-            mx = col_max(mx);
-            const float mn = fmaxf(m_run[rb], mx);
-            if (__builtin_amdgcn_ballot_w64(mn > m_run[rb])) {
-                const float alpha = m_run[rb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
-                l_lane[rb] *= alpha;
+        };
+        if (t0 + 31 <= pos_min) softmax(std::integral_constant<bool, true>{});
+        else softmax(std::integral_constant<bool, false>{});
+        // the accumulators' rescale, shared by both paths (only when some row's max moved)
 #pragma unroll
-                for (int d = 0; d < NDB; ++d) o[rb][d] *= alpha;
-            }
-            m_run[rb] = mn;
-            float psum = 0.0f;
+        for (int rb = 0; rb < NRB; ++rb)
+            if (moved[rb]) {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float pv = sv[jj] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[jj] - mn);
-                psum += pv;
-                pb[rb][jj] = (half_t)pv;
+                for (int d = 0; d < NDB; ++d) o[rb][d] *= alpha[rb];
             }
-            l_lane[rb] += psum;
-        }
 
         // ---- O^T [dim][row] += V^T P^T (tokens past the sequence end zeroed)
         {
