@@ -110,20 +110,30 @@ __device__ __forceinline__ float col_sum(float v) {
     return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
-// One workgroup per (sequence, unit, KV head of the unit, block of 128 query rows,
-// key split): wave w owns rows 32 w .. 32 w + 31 as two 16-row blocks, which share
-// every K and V fragment the wave reads; the key tiles of split sp are
-// [sp tps, (sp + 1) tps) up to the block's causal end.
+// One workgroup of 8 waves per (sequence, unit, KV head of the unit, block of 128
+// query rows, key split); the key tiles of split sp are [sp tps, (sp + 1) tps) up
+// to the block's causal end. Waves 4..7 (producers) load the latent tiles and
+// rebuild the rotated keys of tile k into LDS while waves 0..3 (consumers) run
+// scores, softmax and values of tile k - 1: one barrier per tile, and each SIMD
+// holds one wave of each role, so one's MFMAs run under the other's vector work.
+// Consumer wave w owns query rows 32 w .. 32 w + 31 as two 16-row blocks, which
+// share every K and V fragment it reads; producer wave p owns dims
+// 16 p .. 16 p + 15 and their RoPE partners 64 + 16 p .., loads key rows
+// 8 p .. 8 p + 7 and value dims 64 p .. 64 p + 63 of each tile.
+// LDS: keys three tiles deep (tile k read, k + 1 landed, k + 2 landing), values
+// three deep (tile k - 1 read, k landed, k + 1 landing), rotated K two deep.
 template <int R>
-__global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_attn(const PrefillArgs a) {
     constexpr int DH = 128, KS = R / 16, NDB = R / 16, NRB = 2;
     static_assert(R == 256, "prefill kernel covers rank 256");
-    __shared__ __attribute__((aligned(1024))) half_t htile[2][32 * R];    // H^k [token][rank], chunks swizzled
-    __shared__ __attribute__((aligned(1024))) half_t vtile[2][R * 32];    // H^v [rank][token], chunks swizzled
-    __shared__ __attribute__((aligned(16))) half_t krot[32 * DH];         // K [token][dim], chunks swizzled
+    __shared__ __attribute__((aligned(1024))) half_t htile[3][32 * R];    // H^k [token][rank], chunks swizzled
+    __shared__ __attribute__((aligned(1024))) half_t vtile[3][R * 32];    // H^v [rank][token], chunks swizzled
+    __shared__ __attribute__((aligned(16))) half_t krot[2][32 * DH];      // K [token][dim], chunks swizzled
     __shared__ float2 tokb[DH / 2][32];                                   // (cos, sin)(tau theta_f), tau < 32
 
-    const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const bool producer = wid >= 4;
+    const int wv = wid & 3;
     const int c = l & 15, g = l >> 4;
     int blk = blockIdx.x;
     const int sp = blk % a.n_split;
@@ -139,28 +149,21 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
     const int rows = a.M * a.gq;
     const int row0 = qb * 128;
     if (len <= 0 || row0 >= rows) return;
+    const int m_last = (min(rows, row0 + 128) - 1) / a.gq;
+    const int n_t = min(a.n_tiles, qpos(a.p0, a.lens, b, m_last) / 32 + 1);
+    const int t_beg = sp * a.tps, t_end = min(n_t, t_beg + a.tps);
 
-    // the lane's query rows (column c of the wave's two score blocks)
+    // the consumer lane's query rows (column c of the wave's two score blocks)
     int m_row[NRB], j_row[NRB], pos[NRB];
     bool row_ok[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
         const int rho = row0 + 32 * wv + 16 * rb + c;
-        row_ok[rb] = rho < rows;
+        row_ok[rb] = !producer && rho < rows;
         m_row[rb] = row_ok[rb] ? rho / a.gq : 0;
         j_row[rb] = (u * a.s + w) * a.gq + (row_ok[rb] ? rho % a.gq : 0);
         pos[rb] = row_ok[rb] ? qpos(a.p0, a.lens, b, m_row[rb]) : -1;
     }
-    // the wave's smallest row position (-1 if it holds a row past the chunk): key
-    // tiles ending at or before it are visible to all of the wave's rows
-    int pos_min = min(pos[0], pos[1]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o, kWave));
-    pos_min = __builtin_amdgcn_readfirstlane(pos_min);
-    const int m_last = (min(rows, row0 + 128) - 1) / a.gq;
-    const int n_t = min(a.n_tiles, qpos(a.p0, a.lens, b, m_last) / 32 + 1);
-    const int t_beg = sp * a.tps, t_end = min(n_t, t_beg + a.tps);
-
     auto part_of = [&](int rb) {
         return a.part + (((long)(b * a.M + m_row[rb]) * Hq + j_row[rb]) * a.n_split + sp) * (R + 2);
     };
@@ -177,39 +180,110 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
         return;
     }
 
-    const long bu = (long)b * a.U + u;
-    const half_t* hk = a.hk + bu * a.cap * R;
-    const half_t* hv = a.hv + bu * a.cap * R;
-    auto vswz = [](int d) { return (((d >> 1) ^ (d >> 3)) & 1) | (((d >> 2) & 1) << 1); };
-    const uint32_t kx = 512u * (l >> 5) + 16u * ((l & 31) ^ (l >> 5));
-    const uint32_t vx = 16u * (l ^ vswz(l >> 2));
-    // wave wv loads key rows 8 wv .. 8 wv + 7 and value dims 64 wv .. 64 wv + 63 of tile t
-    auto issue = [&](int t) {
-        const int t0 = 32 * t;
-        const int r0 = t0 + 8 * wv;
-        const int32x4 kr = make_rsrc(hk + (long)r0 * R, (uint32_t)max(0, len - r0) * (R * 2));
-        const int32x4 vr = make_rsrc(hv + (long)(t0 / 32) * R * 32 + 4 * wv * 512, 4096u);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            buf_dma16(kr, (kx ^ (16u * (8 * (wv & 1) + 2 * n))) + 1024u * n, htile[t & 1] + (8 * wv + 2 * n) * R);
-            buf_dma16(vr, vx + 1024u * n, vtile[t & 1] + (4 * wv + n) * 512);
-        }
-    };
-    issue(t_beg);
+    // in-tile offsets (cos, sin)(tau theta_f) to LDS, frequency-major (the 32 lanes
+    // of a frequency read 32 consecutive entries)
+    for (int e = tid; e < 32 * (DH / 2); e += 512)
+        tokb[e % (DH / 2)][e / (DH / 2)] = a.ang[(long)a.n_tiles * (DH / 2) + e];
+    const int n = t_end - t_beg;
 
-    // B^T fragments: A operand of K^T = B^T H^T. Row m of the wave's 32 dims is
-    // dim 16 wv + m (m < 16) or 64 + 16 wv + m - 16; K step ks covers ranks
-    // 16 ks + 8 (l / 32) .. + 7.
-    half8 bf[KS];
-    {
-        const int m = l & 31;
-        const int dim = m < 16 ? 16 * wv + m : 64 + 16 * wv + (m - 16);
-        const half_t* col = a.bk + (long)u * R * (a.s * DH) + w * DH + dim;
+    if (producer) {
+        const long bu = (long)b * a.U + u;
+        const half_t* hk = a.hk + bu * a.cap * R;
+        const half_t* hv = a.hv + bu * a.cap * R;
+        auto vswz = [](int d) { return (((d >> 1) ^ (d >> 3)) & 1) | (((d >> 2) & 1) << 1); };
+        const uint32_t kx = 512u * (l >> 5) + 16u * ((l & 31) ^ (l >> 5));
+        const uint32_t vx = 16u * (l ^ vswz(l >> 2));
+        // four loads each; past t_end the resource is empty (the loads read zero),
+        // which keeps the count per iteration fixed at eight
+        auto issue_keys = [&](int t, int buf) {
+            const int r0 = 32 * t + 8 * wv;
+            const uint32_t bytes = t < t_end ? (uint32_t)max(0, len - r0) * (R * 2) : 0u;
+            const int32x4 kr = make_rsrc(hk + (long)min(r0, a.cap) * R, bytes);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int q = 0; q < 4; ++q)
+                buf_dma16(kr, (kx ^ (16u * (8 * (wv & 1) + 2 * q))) + 1024u * q, htile[buf] + (8 * wv + 2 * q) * R);
+        };
+        auto issue_values = [&](int t, int buf) {
+            const int32x4 vr = make_rsrc(hv + (long)min(t, a.cap / 32) * R * 32 + 4 * wv * 512,
+                                         t < t_end ? 4096u : 0u);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bf[ks][e] = col[(long)(16 * ks + 8 * (l >> 5) + e) * (a.s * DH)];
+            for (int q = 0; q < 4; ++q) buf_dma16(vr, vx + 1024u * q, vtile[buf] + (4 * wv + q) * 512);
+        };
+        // B^T fragments: A operand of K^T = B^T H^T. Row m of the wave's 32 dims is
+        // dim 16 wv + m (m < 16) or 64 + 16 wv + m - 16; K step ks covers ranks
+        // 16 ks + 8 (l / 32) .. + 7.
+        half8 bf[KS];
+        {
+            const int m = l & 31;
+            const int dim = m < 16 ? 16 * wv + m : 64 + 16 * wv + (m - 16);
+            const half_t* col = a.bk + (long)u * R * (a.s * DH) + w * DH + dim;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bf[ks][e] = col[(long)(16 * ks + 8 * (l >> 5) + e) * (a.s * DH)];
+        }
+        // the lane's token is tau = l % 32 and its eight frequencies
+        // f_i = 16 wv + 8 (i / 4) + 4 (l / 32) + i % 4
+        auto freq = [&](int i) { return 16 * wv + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3); };
+        // key fragment of the reconstruction (B operand): token l % 32, ranks 16 ks + 8 (l/32)
+        auto koff = [&](int ks) { return (l & 31) * R + 8 * ((2 * (ks & 7) + (l >> 5)) ^ (l & 15)) + 128 * (ks >> 3); };
+        // (cos, sin) of the tile start for the lane's frequencies, loaded one tile ahead
+        float2 st[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)t_beg * (DH / 2) + freq(i)];
+
+        issue_keys(t_beg, 0);
+        issue_keys(t_beg + 1, 1);
+        issue_values(t_beg, 0);
+        // keys of t_beg complete: the eight loads issued after them may be in flight
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __syncthreads();
+        for (int k = 0; k <= n; ++k) {
+            if (k < n) {
+                // ---- K^T of tile t_beg + k for the wave's 32 dims, RoPE, K to LDS
+                const half_t* ht = htile[k % 3];
+                floatx16 acc = floatx16{};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) acc = mfma32(bf[ks], lds8(ht + koff(ks)), acc);
+                const int tl = l & 31;
+                half_t* kr = krot[k & 1];
+#pragma unroll
+                for (int gi = 0; gi < 2; ++gi) {
+                    half_t lh[4], hh[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * gi + e;
+                        const float2 tk = tokb[freq(i)][tl];
+                        const float cc = st[i].x * tk.x - st[i].y * tk.y;
+                        const float ss = st[i].x * tk.y + st[i].y * tk.x;
+                        const float lo = acc[i], hi = acc[i + 8];
+                        lh[e] = (half_t)(lo * cc - hi * ss);
+                        hh[e] = (half_t)(hi * cc + lo * ss);
+                    }
+                    // dims 16 wv + 8 gi + 4 (l/32) + e (chunk 2 wv + gi) and their partners (+64)
+                    const int q_lo = (2 * wv + gi) ^ (tl & 15), q_hi = (8 + 2 * wv + gi) ^ (tl & 15);
+                    *reinterpret_cast<half4*>(&kr[tl * DH + 8 * q_lo + 4 * (l >> 5)]) = half4{lh[0], lh[1], lh[2], lh[3]};
+                    *reinterpret_cast<half4*>(&kr[tl * DH + 8 * q_hi + 4 * (l >> 5)]) = half4{hh[0], hh[1], hh[2], hh[3]};
+                }
+                if (k + 1 < n) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)(t_beg + k + 1) * (DH / 2) + freq(i)];
+                }
+            }
+            // every LDS read of this iteration done before the DMA may reuse a buffer
+            // (the key buffer taken here was last read in iteration k - 1)
+            issue_keys(t_beg + k + 2, (k + 2) % 3);
+            issue_values(t_beg + k + 1, (k + 1) % 3);
+            // what the next iteration reads (keys of tile k + 1, values of tile k) has
+            // landed: only this iteration's eight loads may still be in flight
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            __syncthreads();
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
     }
+
+    // ---- consumers
     // queries of the lane's rows, dims 32 ks + 8 g + e, in fp16
     half8 qh[NRB][4];
 #pragma unroll
@@ -218,18 +292,15 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qh[rb][ks][e] = (half_t)(row_ok[rb] ? qs[32 * ks + 8 * g + e] : 0.0f);
-            }
+            for (int e = 0; e < 8; ++e) qh[rb][ks][e] = (half_t)(row_ok[rb] ? qs[32 * ks + 8 * g + e] : 0.0f);
     }
-    // in-tile offsets (cos, sin)(tau theta_f) to LDS, frequency-major (the 32 lanes
-    // of a frequency read 32 consecutive entries); the lane's token is tau = l % 32
-    // and its eight frequencies f_i = 16 wv + 8 (i / 4) + 4 (l / 32) + i % 4
-    for (int e = tid; e < 32 * (DH / 2); e += 256)
-        tokb[e % (DH / 2)][e / (DH / 2)] = a.ang[(long)a.n_tiles * (DH / 2) + e];
-    auto freq = [&](int i) { return 16 * wv + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3); };
-    // key fragment of the reconstruction (B operand): token l % 32, ranks 16 ks + 8 (l/32)
-    auto koff = [&](int ks) { return (l & 31) * R + 8 * ((2 * (ks & 7) + (l >> 5)) ^ (l & 15)) + 128 * (ks >> 3); };
+    // the wave's smallest row position (-1 if it holds a row past the chunk): key
+    // tiles ending at or before it are visible to all of the wave's rows
+    int pos_min = min(pos[0], pos[1]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o, kWave));
+    pos_min = __builtin_amdgcn_readfirstlane(pos_min);
+    auto vswz = [](int d) { return (((d >> 1) ^ (d >> 3)) & 1) | (((d >> 2) & 1) << 1); };
     const int vro = 8 * (4 * (l & 15) + ((l >> 4) ^ vswz(l & 15)));
 
     float m_run[NRB], l_lane[NRB];
@@ -241,62 +312,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 #pragma unroll
         for (int d = 0; d < NDB; ++d) o[rb][d] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-
-    // (cos, sin) of the tile start for the lane's frequencies: loaded one tile ahead
-    float2 st[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)t_beg * (DH / 2) + freq(i)];
-    // B^T fragments and queries stay in the AGPRs for the whole loop, where the
-    // MFMAs read them in place (the accumulators and the vector work use the
-    // arithmetic registers); pinned once every load above has been issued
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(bf[ks]));
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qh[rb][ks]));
-    for (int t = t_beg; t < t_end; ++t) {
-        const int t0 = 32 * t;
-        // vmcnt(0) as a builtin: the compiler sees it, so it inserts no later wait for
-        // its own loads (which would also stall on the next tile's loads below)
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();                      // tile t in LDS; tile t-1 fully consumed
-        if (t + 1 < t_end) issue(t + 1);
-
-        // ---- K^T for the wave's 32 dims, RoPE, K to LDS
-        {
-            const half_t* ht = htile[t & 1];
-            floatx16 acc = floatx16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = mfma32(bf[ks], lds8(ht + koff(ks)), acc);
-            const int tl = l & 31;
-#pragma unroll
-            for (int gi = 0; gi < 2; ++gi) {
-                half_t lh[4], hh[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * gi + e;
-                    const float2 tk = tokb[freq(i)][tl];
-                    const float cc = st[i].x * tk.x - st[i].y * tk.y;
-                    const float ss = st[i].x * tk.y + st[i].y * tk.x;
-                    const float lo = acc[i], hi = acc[i + 8];
-                    const float lo2 = lo * cc - hi * ss, hi2 = hi * cc + lo * ss;
-                    lh[e] = (half_t)lo2;
-                    hh[e] = (half_t)hi2;
-                }
-                // dims 16 wv + 8 gi + 4 (l/32) + e (chunk 2 wv + gi) and their partners (+64)
-                const int q_lo = (2 * wv + gi) ^ (tl & 15), q_hi = (8 + 2 * wv + gi) ^ (tl & 15);
-                const int o_lo = tl * DH + 8 * q_lo + 4 * (l >> 5), o_hi = tl * DH + 8 * q_hi + 4 * (l >> 5);
-                *reinterpret_cast<half4*>(&krot[o_lo]) = half4{lh[0], lh[1], lh[2], lh[3]};
-                *reinterpret_cast<half4*>(&krot[o_hi]) = half4{hh[0], hh[1], hh[2], hh[3]};
-            }
-        }
-        if (t + 1 < t_end) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) st[i] = a.ang[(long)(t + 1) * (DH / 2) + freq(i)];
-        }
-        __syncthreads();                      // K of tile t complete
+    __syncthreads();
+    __syncthreads();                          // iteration 0: the producers rebuild the first tile
+    for (int k = 1; k <= n; ++k) {
+        const int t0 = 32 * (t_beg + k - 1);
+        const half_t* kr = krot[(k - 1) & 1];
 
         // ---- S^T [token][row] for both row blocks: block mb row m is token
         // 8 (m/4) + 4 mb + m % 4; four chains
@@ -311,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const int tk = 8 * (c >> 2) + 4 * mb + (c & 3);
-                kh[mb] = lds8(&krot[tk * DH + 8 * ((4 * ks + g) ^ (tk & 15))]);
+                kh[mb] = lds8(&kr[tk * DH + 8 * ((4 * ks + g) ^ (tk & 15))]);
             }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
@@ -366,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
 
         // ---- O^T [dim][row] += V^T P^T (tokens past the sequence end zeroed)
         {
-            const half_t* vt = vtile[t & 1] + vro;
+            const half_t* vt = vtile[(k - 1) % 3] + vro;
             const bool tail = t0 + 32 > len;
             const int first = t0 + 8 * (l >> 4);
 #pragma unroll
@@ -381,6 +401,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn(const PrefillArgs a) {
                 for (int rb = 0; rb < NRB; ++rb) o[rb][d] = mfma16(va, pb[rb], o[rb][d]);
             }
         }
+        __syncthreads();
     }
 
     // the split's state per row: lane (c, g) holds dims 16 d + 4 g + i of row c
@@ -440,7 +461,7 @@ int32_t launch_prefill(const lrkv_latent_cache* c, const float* q, const half_t*
     PrefillArgs a{(const half_t*)c->hk, (const half_t*)c->hv, bk, p0, c->lens, qr, ang, part,
                   c->batch, c->units, c->kv_per_unit, c->q_per_kv, M, c->capacity, n_tiles, n_qb, n_split, tps};
     const long blocks = (long)c->batch * c->units * c->kv_per_unit * n_qb * n_split;
-    hipLaunchKernelGGL(prefill_attn<256>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(prefill_attn<256>, dim3((unsigned)blocks), dim3(512), 0, st, a);
     launch_merge(part, out, c->batch * M * Hq, n_split, R, st);
     return last_launch_status();
 }
