@@ -135,13 +135,22 @@ __global__ __launch_bounds__(512, 1) void prefill_attn(const PrefillArgs a) {
     const bool producer = wid >= 4;
     const int wv = wid & 3;
     const int c = l & 15, g = l >> 4;
-    int blk = blockIdx.x;
-    const int sp = blk % a.n_split;
-    blk /= a.n_split;
+    // Logical block = (sequence, unit, split, KV head, row block), row block
+    // fastest. Workgroups go to the 8 XCDs in turn, so consecutive logical blocks
+    // are spread back onto one XCD: the s x n_qb workgroups that read the same
+    // (unit, split) latents then share that XCD's L2 (one HBM read instead of one
+    // per XCD they were spread over).
+    int blk;
+    {
+        const int nb = gridDim.x, per = nb / 8, rem = nb % 8, x = blockIdx.x % 8, j = blockIdx.x / 8;
+        blk = x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+    }
     const int qb = blk % a.n_qb;
     blk /= a.n_qb;
     const int w = blk % a.s;
     blk /= a.s;
+    const int sp = blk % a.n_split;
+    blk /= a.n_split;
     const int u = blk % a.U, b = blk / a.U;
     if (b >= a.B) return;
     const int Hq = a.U * a.s * a.gq;
