@@ -376,7 +376,9 @@ int32_t lrkv_paged_plan(const lrkv_paged_cache *cache, const int32_t *host_lens,
  * latent-space output o = p H^v). The m_tokens new tokens of each sequence
  * must already be appended (lrkv_append_latent): token m of sequence b sits at
  * position p0[b] + m, and its queries attend causally to tokens 0 .. p0[b] + m
- * (positions are clamped to 0 .. lens[b] - 1).
+ * (positions are clamped to 0 .. lens[b] - 1). Arithmetic: the rotated
+ * queries and the rebuilt, rotated keys are each rounded once to fp16 for the
+ * score products, p once to fp16 for the value product; accumulation in fp32.
  *
  *   cache    lrkv_latent_cache with fp16 latents, rank 256, head_dim 128 (any
  *            kv_per_unit and q_per_kv; LRKV_ERR_UNSUPPORTED otherwise)
