@@ -34,7 +34,8 @@ def _setup(seed, B, U, s, gq, T_end, cap):
 
 @pytest.mark.parametrize("B,U,s,gq,T0,M,cap", [(2, 2, 4, 1, 300, 100, 512), (1, 2, 2, 2, 64, 40, 128),
                                                 (2, 1, 4, 1, 0, 77, 96), (1, 1, 2, 2, 1000, 1, 1024),
-                                                (1, 1, 4, 1, 31, 129, 192)])
+                                                (1, 1, 4, 1, 31, 129, 192), (1, 2, 2, 4, 500, 70, 640),
+                                                (1, 1, 2, 4, 3000, 200, 3264)])
 def test_prefill_parity(B, U, s, gq, T0, M, cap):
     """A chunk of M tokens appended after T0 cached ones (all sequences at the same
     length), causal attention of every chunk query against the oracle on the stored
