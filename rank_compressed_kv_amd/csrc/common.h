@@ -39,14 +39,6 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
 }
 
 // ---------------------------------------------------------------- lane helpers
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
-template <int W>
-__device__ __forceinline__ float reduce_max_width(float v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
 template <int W>
 __device__ __forceinline__ float reduce_sum_width(float v) {
 #pragma unroll

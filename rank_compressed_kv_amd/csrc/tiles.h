@@ -37,25 +37,7 @@ __device__ __forceinline__ float half_max32(float v) {
 }
 
 // ---------------------------------------------------------------- direct global->LDS loads
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
-
-// One 16-byte load per active lane; lane i of the wave writes dst + 16 i. `dst`
-// must be built from wave-uniform values only.
-__device__ __forceinline__ void dma16(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst, 16, 0, 0);
-}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// The same load issued as inline assembly, so that the compiler does not treat
-// it as a store to LDS: it then inserts no vmcnt waits before later LDS reads,
-// and the caller orders the data itself (counted s_waitcnt vmcnt + barrier).
-// `dst` must be wave-uniform; M0 carries its LDS byte address.
-__device__ __forceinline__ void dma16_async(const void* src, const void* dst) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "{m0}"(lds), "v"(src) : "memory");
-}
 
 // Raw buffer resource over [base, base + bytes): loads at or past `bytes` read
 // as zero. Word 3 is the gfx9 raw 32-bit data format. Built from wave-uniform
