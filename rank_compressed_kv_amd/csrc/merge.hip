@@ -69,7 +69,44 @@ __global__ __launch_bounds__(64) void merge_splits(const float* __restrict__ par
     out[bj * D + d] = ((n0 + n1) + (n2 + n3)) * rden;
 }
 
+// The same merge for many rows and at most 64 chunks (the prefill's key splits):
+// four waves per workgroup, one (row, 64 output dims) per wave; lane c holds
+// chunk c's (max, sum) in registers, the weights are broadcast by shuffles.
+__global__ __launch_bounds__(256) void merge_rows(const float* __restrict__ part, float* __restrict__ out,
+                                                  int n_split, int D, long n_items) {
+    const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= n_items) return;
+    const int nd = (D + 63) / 64;
+    const long bj = item / nd;
+    const int lane = threadIdx.x & 63, d = (int)(item % nd) * 64 + lane;
+    const float* pp = part + bj * n_split * (D + 2);
+    const float m = lane < n_split ? pp[(long)lane * (D + 2)] : -INFINITY;
+    const float l = lane < n_split ? pp[(long)lane * (D + 2) + 1] : 0.0f;
+    float mx = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    const float wgt = m == -INFINITY ? 0.0f : exp2f(m - mx);
+    const float den = reduce_sum_width<64>(wgt * l);
+    float num = 0.0f;
+    for (int c = 0; c < n_split; ++c) {
+        const float wc = __shfl(wgt, c, kWave);            // every lane takes part
+        if (d < D) num = fmaf(wc, pp[(long)c * (D + 2) + 2 + d], num);
+    }
+    if (d < D) out[bj * D + d] = num / den;
+}
+
 }  // namespace
+
+void launch_merge_rows(const float* part, float* out, int BH, int n_split, int D, hipStream_t st) {
+    if (n_split > 64) {
+        hipLaunchKernelGGL(merge_splits, dim3(BH, (D + 63) / 64), dim3(64), 0, st, part, out, n_split, D,
+                           (int32_t*)nullptr, 0, 0);
+        return;
+    }
+    const long n_items = (long)BH * ((D + 63) / 64);
+    hipLaunchKernelGGL(merge_rows, dim3((unsigned)((n_items + 3) / 4)), dim3(256), 0, st, part, out, n_split, D,
+                       n_items);
+}
 
 void launch_merge(const float* part, float* out, int BH, int n_split, int D, hipStream_t st) {
     hipLaunchKernelGGL(merge_splits, dim3(BH, (D + 63) / 64), dim3(64), 0, st, part, out, n_split, D,

@@ -450,7 +450,7 @@ size_t prefill_workspace_bytes(int B, int U, int s, int gq, int M, int DH, int R
            align_up((size_t)B * M * Hq * n_split * (R + 2) * sizeof(float), 256);
 }
 
-void launch_merge(const float* part, float* out, int BH, int n_split, int D, hipStream_t st);
+void launch_merge_rows(const float* part, float* out, int BH, int n_split, int D, hipStream_t st);
 
 int32_t launch_prefill(const lrkv_latent_cache* c, const float* q, const half_t* bk, const int32_t* p0, int M,
                        int n_tiles, float sm_scale, float* out, void* ws, hipStream_t st) {
@@ -471,7 +471,7 @@ int32_t launch_prefill(const lrkv_latent_cache* c, const float* q, const half_t*
                   c->batch, c->units, c->kv_per_unit, c->q_per_kv, M, c->capacity, n_tiles, n_qb, n_split, tps};
     const long blocks = (long)c->batch * c->units * c->kv_per_unit * n_qb * n_split;
     hipLaunchKernelGGL(prefill_attn<256>, dim3((unsigned)blocks), dim3(512), 0, st, a);
-    launch_merge(part, out, c->batch * M * Hq, n_split, R, st);
+    launch_merge_rows(part, out, c->batch * M * Hq, n_split, R, st);
     return last_launch_status();
 }
 
