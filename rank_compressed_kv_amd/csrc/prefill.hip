@@ -6,25 +6,26 @@
 //
 // With many queries per token the reconstruction is shared by all of them, so
 // it is done as a GEMM per 32-token key tile (no query-rotated basis): one
-// workgroup of 4 waves per (sequence, unit, KV head of the unit, block of 128
-// query rows, key split), a query row being one (token, query head) pair of that
-// KV head; the splits' (max, sum, output) states are combined by the split-K
-// merge of the decode path. Per key tile:
-//   K^T [dim][token] = B^T H^T   32x32x16 MFMA, wave w owning dims
-//                                16 w .. 16 w + 15 and their RoPE partners
-//                                64 + 16 w .. (B^T fragments in registers), so a
+// workgroup of 8 waves (four producers, four consumers, see prefill_attn) per
+// (sequence, unit, KV head of the unit, block of 128 query rows, key split), a
+// query row being one (token, query head) pair of that KV head; the splits'
+// (max, sum, output) states are combined by a split-K merge. Per key tile:
+//   K^T [dim][token] = B^T H^T   32x32x16 MFMA, producer p owning dims
+//                                16 p .. 16 p + 15 and their RoPE partners
+//                                64 + 16 p .. (B^T fragments in registers), so a
 //                                lane holds both halves of each rotated pair;
 //   RoPE at each token's position in registers, (cos, sin) = tile start x
 //   in-tile offset (both fp64-reduced by the prepare kernel); K written to LDS
 //   in fp16 (queries too: the fp16 rounding of p for the value product already
 //   bounds the output error, and splitting K and q into hi + lo pairs was
 //   measured to change it by less than 15%);
-//   S^T [token][row] = K Q^T     16x16x32 MFMA, wave w owning 32 query rows,
+//   S^T [token][row] = K Q^T     16x16x32 MFMA, consumer w owning 32 query rows,
 //                                rows of K permuted so that a lane's output is 8
 //                                consecutive tokens of one query row;
 //   causal mask, online softmax (log2 domain; queries pre-scaled);
 //   O^T [dim][row] += V^T P^T    16x16x32 MFMA over the dim-major value block.
-// Key and value tiles go buffer->LDS, one tile ahead; two barriers per tile.
+// Key tiles go buffer->LDS two tiles ahead of their reconstruction, value tiles
+// one tile ahead of their product; one barrier per tile.
 #include "tiles.h"
 
 #include <math.h>
